@@ -1,0 +1,129 @@
+"""Seeded synthetic workloads for decode attention.
+
+This module only draws inputs; it holds none of the attention arithmetic. Both
+sides of every parity check (the fp64 oracle and the HIP library) are fed from
+here, and the benchmark uses the same recipe.
+
+Recipe: a ``torch.Generator`` seeded with the workload's seed draws N(0,1)
+float32 values, which are rounded to bf16 (round-to-nearest-even, torch's
+``.to(torch.bfloat16)``). Draw order: for ragged workloads the sequence lengths
+first (uniform integers), then the query tensors, then the cache tensors (MLA:
+q_lat, q_rope, cache; GQA: q, k, v). Cache rows beyond a sequence's length are
+drawn like the rest (they are never read as valid rows).
+
+Shapes follow the source pages' DeepSeek-V3-like geometry ("Mla Analysis"
+skill page, "Cost Models" and "Tensor Shapes": h=128, k=512, p=64, t=4096,
+b=32 for the timing table) and the 64-query/8-KV-head GQA example ("MHA vs GQA
+70B" Q&A page, section 3). The pages use no public dataset.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class MLAShape:
+    b: int
+    s: int
+    h: int
+    k: int
+    p: int
+    t_max: int
+    scale: float
+    seed: int
+    ragged: tuple | None = None  # (low, high) inclusive range of seqlens, or None for full length
+
+    @property
+    def rows(self) -> int:
+        return self.b * self.s * self.h
+
+
+@dataclass(frozen=True)
+class GQAShape:
+    b: int
+    s: int
+    hq: int
+    hkv: int
+    d: int
+    t_max: int
+    scale: float
+    seed: int
+    ragged: tuple | None = None
+
+    @property
+    def rows(self) -> int:
+        return self.b * self.s * self.hq
+
+
+# The five workloads. Their names say what they are.
+MLA_TINY = MLAShape(b=1, s=1, h=16, k=64, p=16, t_max=256, scale=1.0 / math.sqrt(48), seed=0)
+GQA_LAYER = GQAShape(b=32, s=1, hq=64, hkv=8, d=128, t_max=4096, scale=1.0 / math.sqrt(128), seed=1)
+MLA_DSV3 = MLAShape(b=32, s=1, h=128, k=512, p=64, t_max=4096, scale=1.0 / math.sqrt(192), seed=2)
+MLA_MTP4 = MLAShape(b=32, s=4, h=128, k=512, p=64, t_max=4096, scale=1.0 / math.sqrt(192), seed=3)
+MLA_RAGGED = MLAShape(b=64, s=1, h=128, k=512, p=64, t_max=32768, scale=1.0 / math.sqrt(192), seed=4,
+                      ragged=(1024, 32768))
+MTP_SWEEP = (1, 2, 4, 8, 16, 32)
+
+
+def mla_mtp(s: int) -> MLAShape:
+    """DeepSeek-V3-like shapes with s draft tokens per sequence (seed 3 for every s)."""
+    return MLAShape(b=32, s=s, h=128, k=512, p=64, t_max=4096, scale=1.0 / math.sqrt(192), seed=3)
+
+
+WORKLOADS = {
+    "mla_tiny": MLA_TINY,
+    "gqa_layer": GQA_LAYER,
+    "mla_dsv3": MLA_DSV3,
+    "mla_mtp4": MLA_MTP4,
+    "mla_ragged": MLA_RAGGED,
+}
+
+
+def _normal_bf16(gen: torch.Generator, shape) -> torch.Tensor:
+    return torch.randn(*shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+
+
+def _seqlens(gen: torch.Generator, b: int, t_max: int, ragged) -> torch.Tensor:
+    if ragged is None:
+        return torch.full((b,), t_max, dtype=torch.int32)
+    lo, hi = ragged
+    return torch.randint(lo, hi + 1, (b,), generator=gen, dtype=torch.int64).to(torch.int32)
+
+
+def make_mla(shape: MLAShape, seqlens=None):
+    """Return (q_lat, q_rope, cache, seqlens) as CPU tensors (bf16, bf16, bf16, int32)."""
+    gen = torch.Generator().manual_seed(shape.seed)
+    sl = _seqlens(gen, shape.b, shape.t_max, shape.ragged)
+    if seqlens is not None:
+        sl = torch.as_tensor(seqlens, dtype=torch.int32).clone()
+    q_lat = _normal_bf16(gen, (shape.b, shape.s, shape.h, shape.k))
+    q_rope = _normal_bf16(gen, (shape.b, shape.s, shape.h, shape.p))
+    cache = _normal_bf16(gen, (shape.b, shape.t_max, shape.k + shape.p))
+    return q_lat, q_rope, cache, sl
+
+
+def make_gqa(shape: GQAShape, seqlens=None):
+    """Return (q, k, v, seqlens) as CPU tensors (bf16 x3, int32)."""
+    gen = torch.Generator().manual_seed(shape.seed)
+    sl = _seqlens(gen, shape.b, shape.t_max, shape.ragged)
+    if seqlens is not None:
+        sl = torch.as_tensor(seqlens, dtype=torch.int32).clone()
+    q = _normal_bf16(gen, (shape.b, shape.s, shape.hq, shape.d))
+    k = _normal_bf16(gen, (shape.b, shape.t_max, shape.hkv, shape.d))
+    v = _normal_bf16(gen, (shape.b, shape.t_max, shape.hkv, shape.d))
+    return q, k, v, sl
+
+
+def sample_rows(total_rows: int, n: int, seed: int) -> torch.Tensor:
+    """A fixed, seeded sample of n distinct flattened row ids (sorted), always
+    including the first and last row."""
+    n = min(n, total_rows)
+    gen = torch.Generator().manual_seed(1000 + seed)
+    idx = torch.randperm(total_rows, generator=gen)[:n]
+    idx[0] = 0
+    if n > 1:
+        idx[1] = total_rows - 1
+    return torch.unique(idx).to(torch.int64)
