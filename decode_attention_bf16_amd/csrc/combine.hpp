@@ -1,0 +1,58 @@
+// Log-sum-exp combine of split-KV partial results.
+//
+// A sequence whose cache rows were split over several workers has one partial
+// (out_r normalized by its own softmax sum, lse_r in log2 units) per segment.
+// The merged result is lse = log(sum_r 2^lse_r) and out = sum_r 2^(lse_r - lse)
+// out_r, which equals softmax attention over the union of the segments' rows.
+// Empty segments carry lse_r = -inf and weigh nothing. Sequences with no cache
+// row at all (no segment) get out = 0, lse = -inf here; sequences with a
+// single segment were written by their worker and are skipped.
+#pragma once
+
+#include "common.hpp"
+
+namespace da {
+
+// One wave per query row; DV output columns spread over the 64 lanes.
+template <int DV>
+__global__ void __launch_bounds__(256) combine_kernel(int B, int M, const int *__restrict__ slot_start,
+                                                      const float *__restrict__ part_out,
+                                                      const float *__restrict__ part_lse,
+                                                      uint16_t *__restrict__ out, float *__restrict__ lse)
+{
+    static_assert(DV % 64 == 0, "columns per lane");
+    constexpr int CPL = DV / 64;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const long row_g = (long)blockIdx.x * 4 + wave;
+    if (row_g >= (long)B * M) return;
+    const int bq = (int)(row_g / M);
+    const int row = (int)(row_g - (long)bq * M);
+    const int s0 = slot_start[bq];
+    const int nseg = slot_start[bq + 1] - s0;
+    if (nseg == 1) return;
+
+    float m = -INFINITY;
+    for (int r = 0; r < nseg; ++r) m = fmaxf(m, part_lse[(size_t)(s0 + r) * M + row]);
+
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+        for (int r = 0; r < nseg; ++r) {
+            const float wgt = fast_exp2(part_lse[(size_t)(s0 + r) * M + row] - m);
+            wsum += wgt;
+            const float *src = part_out + ((size_t)(s0 + r) * M + row) * DV + lane * CPL;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[c] += wgt * src[c];
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    uint16_t *dst = out + (size_t)row_g * DV + lane * CPL;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) dst[c] = to_bf16_bits(acc[c] * inv);
+    if (lane == 0) lse[row_g] = wsum > 0.f ? (m + fast_log2(wsum)) * kLn2 : -INFINITY;
+}
+
+}  // namespace da

@@ -1,0 +1,123 @@
+// Shared device helpers for the gfx950 decode-attention kernels: vector types,
+// bf16 packing, MFMA and LDS-transpose wrappers, DPP reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace da {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+#define DA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Lazy softmax rescale: the running reference maximum is only moved when a new
+// score exceeds it by more than this many powers of two, so unnormalized
+// probabilities stay below 2^kRescaleSlack (harmless in fp32/bf16 range) and
+// the accumulator is rarely rescaled.
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Two floats -> one dword of two bf16 (round to nearest even), lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    __bf16 a = (__bf16)lo;
+    __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(unsigned short, a) |
+           ((uint32_t)__builtin_bit_cast(unsigned short, b) << 16);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float f)
+{
+    __bf16 a = (__bf16)f;
+    return __builtin_bit_cast(unsigned short, a);
+}
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                           false);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes, lane
+// j supplies the address of four consecutive 16-bit elements R[j][0..3]; lane i
+// receives element e = R[4e + i/4][i%4], e = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(p));
+}
+
+// DPP cross-lane moves within a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15 - i within 16
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i within 8
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+
+// Sum over aligned groups of N lanes (N in {8, 16, 32}); every lane of the
+// group receives the full sum. Uses mirror butterflies (each step pairs lanes
+// whose partial sums are disjoint) so the order is fixed.
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(N == 8 || N == 16 || N == 32, "group size");
+    if constexpr (N == 32) v += __shfl_xor(v, 16);
+    if constexpr (N >= 16) v += dpp_f<kDppRowMirror>(v);
+    v += dpp_f<kDppRowHalfMirror>(v);
+    v += dpp_f<kDppQuadXor2>(v);
+    v += dpp_f<kDppQuadXor1>(v);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_across_groups16(float v)
+{
+    // max over lanes l, l^16, l^32, l^48
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_across_groups16(float v)
+{
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ int clamp_len(int len, int t_max)
+{
+    return len < 0 ? 0 : (len > t_max ? t_max : len);
+}
+
+// Round-robin XCD dispatch: block id bid runs on XCD bid % 8. Map it to a
+// linear unit id so that consecutive units share an XCD (and its L2).
+__device__ __forceinline__ int xcd_linear_unit(int bid, int grid)
+{
+    const int per_xcd = grid >> 3;  // grid is a multiple of 8
+    return (bid & 7) * per_xcd + (bid >> 3);
+}
+
+}  // namespace da

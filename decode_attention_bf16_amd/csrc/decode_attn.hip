@@ -1,0 +1,303 @@
+// C ABI of the gfx950 decode-attention library: argument checks, work-partition
+// choice and kernel launches. See include/decode_attn.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+
+#include "../../include/decode_attn.h"
+#include "combine.hpp"
+#include "common.hpp"
+#include "gqa_kernel.hpp"
+#include "mla_kernel.hpp"
+#include "plan.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    int cu_count = 0;
+};
+
+std::mutex g_mutex;
+DeviceInfo g_dev[kMaxDevices];
+
+int current_cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (g_dev[dev].cu_count == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        g_dev[dev].cu_count = cus;
+    }
+    return g_dev[dev].cu_count;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool log_plan()
+{
+    static const bool on = [] {
+        const char *e = getenv("DA_LOG");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+
+// ------------------------------------------------------------------ MLA
+constexpr int kMlaRows = 64;
+
+int mla_row_blocks(int s, int h) { return (s * h + kMlaRows - 1) / kMlaRows; }
+
+int mla_workers(int b, int s, int h, int t_max, int requested)
+{
+    if (requested > 0) return requested;
+    const int rb = mla_row_blocks(s, h);
+    int w = current_cu_count() / rb;
+    if (w < 1) w = 1;
+    // never more workers than tiles could exist
+    const long max_tiles = (long)b * ((t_max + 63) / 64);
+    if ((long)w > max_tiles) w = (int)max_tiles;
+    return w < 1 ? 1 : w;
+}
+
+bool mla_supported(int k, int p)
+{
+    return (k == 512 && p == 64) || (k == 256 && p == 64) || (k == 128 && p == 64) || (k == 64 && p == 16);
+}
+
+template <int K, int P>
+hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *cache, const int32_t *seqlens,
+                      int b, int s, int h, int t_max, float scale_log2, uint16_t *out, float *lse,
+                      const da::WsLayout &ws, char *wsp, int workers, hipStream_t stream)
+{
+    using C = da::MlaCfg<K, P>;
+    static std::once_flag attr_once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(attr_once, [] {
+        attr_err = hipFuncSetAttribute((const void *)da::mla_decode_kernel<K, P>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+
+    auto *hdr = (da::PlanHeader *)(wsp + ws.header);
+    int *tile_start = (int *)(wsp + ws.tile_start);
+    int *slot_start = (int *)(wsp + ws.slot_start);
+    float *part_lse = (float *)(wsp + ws.part_lse);
+    float *part_out = (float *)(wsp + ws.part_out);
+
+    hipLaunchKernelGGL(da::plan_kernel, dim3(1), dim3(da::kPlanThreads), 0, stream, seqlens, b, t_max, C::T, workers,
+                       hdr, tile_start, slot_start);
+    const int rb = mla_row_blocks(s, h);
+    const int units = workers * rb;
+    const int grid = (units + 7) / 8 * 8;
+    if (log_plan())
+        fprintf(stderr, "[decode_attn] mla k=%d p=%d b=%d s=%d h=%d t_max=%d workers=%d row_blocks=%d grid=%d lds=%d\n",
+                K, P, b, s, h, t_max, workers, rb, grid, C::LDS_BYTES);
+    hipLaunchKernelGGL((da::mla_decode_kernel<K, P>), dim3(grid), dim3(256), C::LDS_BYTES, stream, q_lat, q_rope,
+                       cache, seqlens, b, s, h, t_max, scale_log2, rb, units, hdr, tile_start, slot_start, out, lse,
+                       part_out, part_lse);
+    const long rows = (long)b * s * h;
+    hipLaunchKernelGGL(da::combine_kernel<K>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, b, s * h,
+                       slot_start, part_out, part_lse, out, lse);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ GQA
+int gqa_head_blocks(int hkv) { return (hkv + 3) / 4; }
+
+int gqa_workers(int b, int hkv, int t_max, int requested)
+{
+    if (requested > 0) return requested;
+    int w = 2 * current_cu_count() / gqa_head_blocks(hkv);
+    if (w < 1) w = 1;
+    const long max_tiles = (long)b * ((t_max + da::kGqaTile - 1) / da::kGqaTile);
+    if ((long)w > max_tiles) w = (int)max_tiles;
+    return w < 1 ? 1 : w;
+}
+
+bool gqa_valu_ok(int rows) { return rows <= 16; }
+
+template <int D, int R>
+void launch_gqa_valu(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *seqlens, int b, int s,
+                     int hq, int hkv, int t_max, float scale_log2, uint16_t *out, float *lse, da::PlanHeader *hdr,
+                     int *tile_start, int *slot_start, float *part_out, float *part_lse, int workers,
+                     hipStream_t stream)
+{
+    const int hb = gqa_head_blocks(hkv);
+    const int units = workers * hb;
+    const int grid = (units + 7) / 8 * 8;
+    hipLaunchKernelGGL((da::gqa_valu_kernel<D, R>), dim3(grid), dim3(256), 0, stream, q, k, v, seqlens, b, s, hq,
+                       hkv, t_max, scale_log2, hb, units, hdr, tile_start, slot_start, out, lse, part_out,
+                       part_lse);
+}
+
+template <int D>
+bool dispatch_gqa_valu(int rows, const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *seqlens,
+                       int b, int s, int hq, int hkv, int t_max, float scale_log2, uint16_t *out, float *lse,
+                       da::PlanHeader *hdr, int *tile_start, int *slot_start, float *part_out, float *part_lse,
+                       int workers, hipStream_t stream)
+{
+#define DA_GQA_CASE(RR)                                                                                            \
+    if (rows <= RR) {                                                                                              \
+        launch_gqa_valu<D, RR>(q, k, v, seqlens, b, s, hq, hkv, t_max, scale_log2, out, lse, hdr, tile_start,      \
+                               slot_start, part_out, part_lse, workers, stream);                                  \
+        return true;                                                                                               \
+    }
+    DA_GQA_CASE(2)
+    DA_GQA_CASE(4)
+    DA_GQA_CASE(8)
+    DA_GQA_CASE(16)
+#undef DA_GQA_CASE
+    return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+int da_version(void) { return 100; }
+
+const char *da_status_string(da_status status)
+{
+    switch (status) {
+    case DA_OK:
+        return "ok";
+    case DA_ERR_INVALID_ARG:
+        return "invalid argument";
+    case DA_ERR_UNSUPPORTED:
+        return "unsupported dimensions";
+    case DA_ERR_WORKSPACE:
+        return "workspace too small";
+    case DA_ERR_HIP:
+        return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+static da_status mla_check(int b, int s, int h, int k, int p, int t_max, int num_workers)
+{
+    if (b <= 0 || s <= 0 || h <= 0 || k <= 0 || p <= 0 || t_max <= 0 || num_workers < 0) return DA_ERR_INVALID_ARG;
+    if (s > t_max) return DA_ERR_INVALID_ARG;
+    if (!mla_supported(k, p)) return DA_ERR_UNSUPPORTED;
+    if ((long)s * h > 65536) return DA_ERR_UNSUPPORTED;
+    return DA_OK;
+}
+
+size_t mla_decode_workspace_size(int b, int s, int h, int k, int p, int t_max, int num_workers)
+{
+    if (mla_check(b, s, h, k, p, t_max, num_workers) != DA_OK) return 0;
+    const int w = mla_workers(b, s, h, t_max, num_workers);
+    return da::ws_layout(b, s * h, k, w).total;
+}
+
+da_status mla_decode(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *cache, const int32_t *seqlens,
+                     int b, int s, int h, int k, int p, int t_max, float scale, uint16_t *out_lat, float *lse,
+                     void *workspace, size_t workspace_bytes, int num_workers, void *stream)
+{
+    da_status st = mla_check(b, s, h, k, p, t_max, num_workers);
+    if (st != DA_OK) return st;
+    if (!q_lat || !q_rope || !cache || !seqlens || !out_lat || !lse || !workspace) return DA_ERR_INVALID_ARG;
+    if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(cache) || !aligned16(out_lat))
+        return DA_ERR_INVALID_ARG;
+    if (((uintptr_t)workspace & 255u) != 0) return DA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return DA_ERR_INVALID_ARG;
+    const int workers = mla_workers(b, s, h, t_max, num_workers);
+    const da::WsLayout ws = da::ws_layout(b, s * h, k, workers);
+    if (workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
+
+    const float sl2 = scale * da::kLog2e;
+    hipStream_t st_ = (hipStream_t)stream;
+    char *wsp = (char *)workspace;
+    hipError_t e = hipSuccess;
+    if (k == 512 && p == 64)
+        e = launch_mla<512, 64>(q_lat, q_rope, cache, seqlens, b, s, h, t_max, sl2, out_lat, lse, ws, wsp, workers, st_);
+    else if (k == 256 && p == 64)
+        e = launch_mla<256, 64>(q_lat, q_rope, cache, seqlens, b, s, h, t_max, sl2, out_lat, lse, ws, wsp, workers, st_);
+    else if (k == 128 && p == 64)
+        e = launch_mla<128, 64>(q_lat, q_rope, cache, seqlens, b, s, h, t_max, sl2, out_lat, lse, ws, wsp, workers, st_);
+    else
+        e = launch_mla<64, 16>(q_lat, q_rope, cache, seqlens, b, s, h, t_max, sl2, out_lat, lse, ws, wsp, workers, st_);
+    return e == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+static da_status gqa_check(int b, int s, int hq, int hkv, int d, int t_max, int num_workers)
+{
+    if (b <= 0 || s <= 0 || hq <= 0 || hkv <= 0 || d <= 0 || t_max <= 0 || num_workers < 0) return DA_ERR_INVALID_ARG;
+    if (hq % hkv != 0 || s > t_max) return DA_ERR_INVALID_ARG;
+    if (!(d == 64 || d == 128 || d == 256)) return DA_ERR_UNSUPPORTED;
+    if ((hq / hkv) * s > 16) return DA_ERR_UNSUPPORTED;
+    return DA_OK;
+}
+
+size_t gqa_decode_workspace_size(int b, int s, int hq, int hkv, int d, int t_max, int num_workers)
+{
+    if (gqa_check(b, s, hq, hkv, d, t_max, num_workers) != DA_OK) return 0;
+    const int w = gqa_workers(b, hkv, t_max, num_workers);
+    return da::ws_layout(b, s * hq, d, w).total;
+}
+
+da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *seqlens,
+                     int b, int s, int hq, int hkv, int d, int t_max, float scale, uint16_t *out, float *lse,
+                     void *workspace, size_t workspace_bytes, int num_workers, int path, void *stream)
+{
+    da_status st = gqa_check(b, s, hq, hkv, d, t_max, num_workers);
+    if (st != DA_OK) return st;
+    if (path < 0 || path > 2) return DA_ERR_INVALID_ARG;
+    if (path == 2) return DA_ERR_UNSUPPORTED;
+    if (!q || !k_cache || !v_cache || !seqlens || !out || !lse || !workspace) return DA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return DA_ERR_INVALID_ARG;
+    if (((uintptr_t)workspace & 255u) != 0) return DA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return DA_ERR_INVALID_ARG;
+    const int rows = (hq / hkv) * s;
+    if (!gqa_valu_ok(rows)) return DA_ERR_UNSUPPORTED;
+    const int workers = gqa_workers(b, hkv, t_max, num_workers);
+    const da::WsLayout ws = da::ws_layout(b, s * hq, d, workers);
+    if (workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
+
+    char *wsp = (char *)workspace;
+    auto *hdr = (da::PlanHeader *)(wsp + ws.header);
+    int *tile_start = (int *)(wsp + ws.tile_start);
+    int *slot_start = (int *)(wsp + ws.slot_start);
+    float *part_lse = (float *)(wsp + ws.part_lse);
+    float *part_out = (float *)(wsp + ws.part_out);
+    hipStream_t st_ = (hipStream_t)stream;
+    const float sl2 = scale * da::kLog2e;
+
+    hipLaunchKernelGGL(da::plan_kernel, dim3(1), dim3(da::kPlanThreads), 0, st_, seqlens, b, t_max, da::kGqaTile,
+                       workers, hdr, tile_start, slot_start);
+    if (log_plan())
+        fprintf(stderr, "[decode_attn] gqa d=%d b=%d s=%d hq=%d hkv=%d t_max=%d workers=%d path=valu\n", d, b, s, hq,
+                hkv, t_max, workers);
+    bool ok = false;
+    if (d == 64)
+        ok = dispatch_gqa_valu<64>(rows, q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
+                                   tile_start, slot_start, part_out, part_lse, workers, st_);
+    else if (d == 128)
+        ok = dispatch_gqa_valu<128>(rows, q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
+                                    tile_start, slot_start, part_out, part_lse, workers, st_);
+    else
+        ok = dispatch_gqa_valu<256>(rows, q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
+                                    tile_start, slot_start, part_out, part_lse, workers, st_);
+    if (!ok) return DA_ERR_UNSUPPORTED;
+    const long nrows = (long)b * s * hq;
+    if (d == 64)
+        hipLaunchKernelGGL(da::combine_kernel<64>, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st_, b, s * hq,
+                           slot_start, part_out, part_lse, out, lse);
+    else if (d == 128)
+        hipLaunchKernelGGL(da::combine_kernel<128>, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st_, b, s * hq,
+                           slot_start, part_out, part_lse, out, lse);
+    else
+        hipLaunchKernelGGL(da::combine_kernel<256>, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st_, b, s * hq,
+                           slot_start, part_out, part_lse, out, lse);
+    return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,260 @@
+// Grouped-query decode kernels for gfx950 (MHA / GQA / MQA).
+//
+// The query heads of a sequence form contiguous groups of g = hq/hkv heads and
+// every group reads one K/V head ("Why MLA and MTP Fight Each Other",
+// introduction table: arithmetic intensity hq/hkv; "MHA vs GQA 70B", section 1:
+// 64 query heads over 8 KV heads). With s draft tokens a KV head serves
+// R = g*s query rows. Decode reads each cached K/V row once and does only
+// 4*R*d FLOPs on it, so the kernel is bound by HBM bandwidth: the design goal
+// is to keep 16-byte loads in flight and the per-byte ALU work small.
+//
+// VALU kernel (R <= 16): one wave per (KV head, segment). Lanes are split into
+// NSLOT token slots of D/8 lanes; lane (dg, slot) holds dims 8*dg..8*dg+7 of
+// one token per step (a 16-byte load of K and one of V). Scores: 4 bf16 dot2
+// per row, then a mirror-butterfly DPP sum over the D/8 lanes of the slot.
+// Each slot runs its own online softmax (no cross-slot traffic per step); the
+// slots are merged once at the end of the segment. Values: bf16 dot2 over
+// pairs of tokens (probabilities rounded to bf16, as an MFMA path would).
+#pragma once
+
+#include "common.hpp"
+#include "plan.hpp"
+
+namespace da {
+
+constexpr int kGqaTile = 64;  // planner tile (tokens) for GQA
+
+template <int D, int R>
+struct GqaValuCfg {
+    static_assert(D == 64 || D == 128 || D == 256, "head dim");
+    static constexpr int LPT = D / 8;       // lanes per token
+    static constexpr int NSLOT = 64 / LPT;  // token slots per wave
+    static constexpr int U = 4;             // tokens per slot per step (even)
+    static constexpr int STEP = NSLOT * U;  // tokens per wave step
+    static_assert(kGqaTile % STEP == 0, "tile multiple of step");
+};
+
+template <int D, int R>
+__global__ void __launch_bounds__(256)
+    gqa_valu_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+                    const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens, int B, int s, int hq,
+                    int hkv, int t_max, float scale_log2, int head_blocks, int units,
+                    const PlanHeader *__restrict__ hdr, const int *__restrict__ tile_start,
+                    const int *__restrict__ slot_start, uint16_t *__restrict__ out, float *__restrict__ lse,
+                    float *__restrict__ part_out, float *__restrict__ part_lse)
+{
+    using C = GqaValuCfg<D, R>;
+    const int unit = xcd_linear_unit(blockIdx.x, gridDim.x);
+    if (unit >= units) return;
+    const int worker = unit / head_blocks;
+    const int hb = unit - worker * head_blocks;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int kvh = hb * 4 + wave;
+    if (kvh >= hkv) return;
+
+    const int total = hdr->total_tiles;
+    const int per = hdr->per;
+    const int tile_lo = worker * per;
+    if (tile_lo >= total) return;
+    const int tile_hi = min(total, tile_lo + per);
+
+    const int dg = lane % C::LPT;
+    const int slot = lane / C::LPT;
+    const int grp = hq / hkv;
+    const int Rr = grp * s;  // real rows of this KV head
+    const int M = s * hq;    // query rows per sequence
+    const size_t tok_stride = (size_t)hkv * D;
+
+    uint32_t qv[R][4];
+    float m[R], l[R], acc[R][8];
+    int nvis[R];
+    int nvis_min = 0;
+
+    auto row_of = [&](int r) {  // row within the sequence: (draft i, head kvh*grp + j)
+        const int i = r / grp;
+        const int j = r - i * grp;
+        return i * hq + kvh * grp + j;
+    };
+
+    auto begin_segment = [&](int bq) {
+        const int L = clamp_len(seqlens[bq], t_max);
+        int mn = 0x7fffffff;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (r < Rr) {
+                v = *(const u32x4 *)(q + ((size_t)bq * M + row_of(r)) * D + dg * 8);
+                nvis[r] = L - s + r / grp + 1;
+            } else {
+                nvis[r] = 0;
+            }
+            mn = min(mn, r < Rr ? nvis[r] : mn);
+            qv[r][0] = v[0];
+            qv[r][1] = v[1];
+            qv[r][2] = v[2];
+            qv[r][3] = v[3];
+            m[r] = -INFINITY;
+            l[r] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+        }
+        nvis_min = mn;
+    };
+
+    auto end_segment = [&](int bq, int first_tile_of_seq) {
+        // merge the token slots: common reference max per row
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float mm = m[r];
+            for (int off = C::LPT; off < 64; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
+            const float f = mm == -INFINITY ? 0.f : fast_exp2(m[r] - mm);
+            float lr = l[r] * f;
+            for (int off = C::LPT; off < 64; off <<= 1) lr += __shfl_xor(lr, off);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float a = acc[r][e] * f;
+                for (int off = C::LPT; off < 64; off <<= 1) a += __shfl_xor(a, off);
+                acc[r][e] = a;
+            }
+            m[r] = mm;
+            l[r] = lr;
+        }
+        if (slot != 0) return;
+        const int nseg = slot_start[bq + 1] - slot_start[bq];
+        const bool direct = nseg == 1;
+        const int sl = slot_start[bq] + (worker - first_tile_of_seq / per);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (r >= Rr) continue;
+            const int row = row_of(r);
+            const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
+            const float lse2 = l[r] > 0.f ? m[r] + fast_log2(l[r]) : -INFINITY;
+            if (direct) {
+                u32x4 v;
+                v[0] = pack_bf16x2(acc[r][0] * inv, acc[r][1] * inv);
+                v[1] = pack_bf16x2(acc[r][2] * inv, acc[r][3] * inv);
+                v[2] = pack_bf16x2(acc[r][4] * inv, acc[r][5] * inv);
+                v[3] = pack_bf16x2(acc[r][6] * inv, acc[r][7] * inv);
+                *(u32x4 *)(out + ((size_t)bq * M + row) * D + dg * 8) = v;
+                if (dg == 0) lse[(size_t)bq * M + row] = lse2 * kLn2;
+            } else {
+                float *o = part_out + ((size_t)sl * M + row) * D + dg * 8;
+                *(f32x4 *)o = f32x4{acc[r][0] * inv, acc[r][1] * inv, acc[r][2] * inv, acc[r][3] * inv};
+                *(f32x4 *)(o + 4) = f32x4{acc[r][4] * inv, acc[r][5] * inv, acc[r][6] * inv, acc[r][7] * inv};
+                if (dg == 0) part_lse[(size_t)sl * M + row] = lse2;
+            }
+        }
+    };
+
+    int bcur = find_sequence(tile_start, B, tile_lo);
+    int ts_cur = tile_start[bcur];
+    int te_cur = tile_start[bcur + 1];
+    int L = clamp_len(seqlens[bcur], t_max);
+    begin_segment(bcur);
+
+    for (int tt = tile_lo; tt < tile_hi; ++tt) {
+        if (tt >= te_cur) {
+            end_segment(bcur, ts_cur);
+            bcur = find_sequence(tile_start, B, tt);
+            ts_cur = tile_start[bcur];
+            te_cur = tile_start[bcur + 1];
+            L = clamp_len(seqlens[bcur], t_max);
+            begin_segment(bcur);
+        }
+        const int t_tile = (tt - ts_cur) * kGqaTile;
+        const int t_stop = min(L, t_tile + kGqaTile);
+        const uint16_t *kb = kc + (size_t)bcur * t_max * tok_stride + (size_t)kvh * D + dg * 8;
+        const uint16_t *vb = vc + (size_t)bcur * t_max * tok_stride + (size_t)kvh * D + dg * 8;
+
+        for (int t0 = t_tile; t0 < t_stop; t0 += C::STEP) {
+            u32x4 kk[C::U], vv[C::U];
+#pragma unroll
+            for (int u = 0; u < C::U; ++u) {
+                const int tok = t0 + u * C::NSLOT + slot;
+                kk[u] = u32x4{0u, 0u, 0u, 0u};
+                vv[u] = u32x4{0u, 0u, 0u, 0u};
+                if (tok < t_stop) {
+                    kk[u] = *(const u32x4 *)(kb + (size_t)tok * tok_stride);
+                    vv[u] = *(const u32x4 *)(vb + (size_t)tok * tok_stride);
+                }
+            }
+            // scores
+            float sc[C::U][R];
+#pragma unroll
+            for (int u = 0; u < C::U; ++u) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float d = 0.f;
+                    d = dot2_bf16(qv[r][0], kk[u][0], d);
+                    d = dot2_bf16(qv[r][1], kk[u][1], d);
+                    d = dot2_bf16(qv[r][2], kk[u][2], d);
+                    d = dot2_bf16(qv[r][3], kk[u][3], d);
+                    sc[u][r] = group_sum<C::LPT>(d);
+                }
+            }
+            // mask: tokens past a row's visible end (and past the tile end)
+            if (t0 + C::STEP > nvis_min || t0 + C::STEP > t_stop) {
+#pragma unroll
+                for (int u = 0; u < C::U; ++u) {
+                    const int tok = t0 + u * C::NSLOT + slot;
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        if (tok >= t_stop || tok >= nvis[r]) sc[u][r] = -INFINITY;
+                }
+            }
+            // per-slot online softmax
+            bool need = false;
+            float mt[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float mx = sc[0][r];
+#pragma unroll
+                for (int u = 1; u < C::U; ++u) mx = fmaxf(mx, sc[u][r]);
+                mt[r] = mx * scale_log2;
+                need |= mt[r] > m[r] + kRescaleSlack;
+            }
+            if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float mn = fmaxf(m[r], mt[r]);
+                    const float al = mn == -INFINITY ? 1.f : fast_exp2(m[r] - mn);
+                    m[r] = mn;
+                    l[r] *= al;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[r][e] *= al;
+                }
+            }
+            uint32_t pp[C::U / 2][R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float ms = m[r] == -INFINITY ? 0.f : m[r];
+#pragma unroll
+                for (int u = 0; u < C::U; u += 2) {
+                    const float p0 = fast_exp2(__builtin_fmaf(sc[u][r], scale_log2, -ms));
+                    const float p1 = fast_exp2(__builtin_fmaf(sc[u + 1][r], scale_log2, -ms));
+                    l[r] += p0 + p1;
+                    pp[u / 2][r] = pack_bf16x2(p0, p1);
+                }
+            }
+            // values: pairs of tokens through bf16 dot2
+#pragma unroll
+            for (int u = 0; u < C::U; u += 2) {
+                uint32_t vp[8];
+#pragma unroll
+                for (int dw = 0; dw < 4; ++dw) {
+                    const uint32_t a = vv[u][dw], b2 = vv[u + 1][dw];
+                    vp[2 * dw] = (a & 0xffffu) | (b2 << 16);
+                    vp[2 * dw + 1] = (a >> 16) | (b2 & 0xffff0000u);
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[r][e] = dot2_bf16(pp[u / 2][r], vp[e], acc[r][e]);
+            }
+        }
+    }
+    end_segment(bcur, ts_cur);
+}
+
+}  // namespace da

@@ -1,0 +1,131 @@
+/*
+ * decode_attn.h -- C ABI of the MI355X (gfx950) decode-attention library.
+ *
+ * The library computes the attention core of one autoregressive decode step
+ * over a bf16 KV cache, for s query tokens per sequence (s = 1 plain decode,
+ * s > 1 speculative / multi-token-prediction drafts), in two forms:
+ *
+ *  - mla_decode: multi-head latent attention in absorbed form. The absorbed
+ *    query q_lat = Q.Wk^T scores directly against the cached latent Z, the
+ *    decoupled rope part q_rope scores against the cached rope keys, and the
+ *    output stays in latent space, softmax(.).Z ("Mla Analysis" skill page,
+ *    sections "Absorption Trick (FlashMLA)" and "Tensor Shapes"). Decompressing
+ *    the output through Wv is the caller's separate step.
+ *  - gqa_decode: grouped-query attention, covering MHA (hkv = hq), GQA and MQA
+ *    (hkv = 1); query heads form contiguous groups of hq/hkv that share one K/V
+ *    head ("Why MLA and MTP Fight Each Other", introduction table of attention
+ *    variants; "MQA, GQA & MLA" lesson, Concept section).
+ *
+ * Semantics shared by both entry points
+ *  - Softmax attention per query row: lse = ln(sum_j exp(scale * q.k_j)) over
+ *    the visible cache rows j, out = sum_j exp(scale * q.k_j - lse) * v_j.
+ *  - Draft mask: with L = seqlens[b] clamped to [0, t_max], query token i
+ *    (0 <= i < s) of sequence b sees cache rows 0 .. L - s + i (L counts the
+ *    drafts' own rows). A row that sees no cache row gets out = 0, lse = -inf.
+ *  - lse is in natural-log units, fp32. out is bf16, rounded to nearest even.
+ *  - Arithmetic: bf16 products with fp32 accumulation (MFMA / dot2), fp32
+ *    online softmax. Results are not bitwise identical across split choices.
+ *
+ * Pointers and ownership
+ *  - Every tensor pointer is a DEVICE pointer to contiguous row-major memory;
+ *    bf16 tensors are passed as uint16_t bit patterns. The caller allocates and
+ *    owns every buffer, including the workspace; the library allocates nothing
+ *    per call and keeps only a cached device-property query (thread-safe).
+ *  - `stream` is a hipStream_t (NULL = the default stream). All work is queued
+ *    asynchronously on it; no call synchronizes the host and no call reads
+ *    seqlens on the host. Buffers must stay alive until the stream's work ends.
+ *  - Inputs must not alias outputs or the workspace.
+ *
+ * Errors: a problem the host can see returns a status and queues nothing.
+ *  DA_ERR_INVALID_ARG  null pointer, a dimension <= 0, hq % hkv != 0, s > t_max,
+ *                      num_workers < 0, a non-finite scale.
+ *  DA_ERR_UNSUPPORTED  a dimension outside the compiled set (see each call).
+ *  DA_ERR_WORKSPACE    workspace_bytes below the matching *_workspace_size.
+ *  DA_ERR_HIP          a HIP launch error (the HIP error is cleared).
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DA_OK = 0,
+    DA_ERR_INVALID_ARG = 1,
+    DA_ERR_UNSUPPORTED = 2,
+    DA_ERR_WORKSPACE = 3,
+    DA_ERR_HIP = 4
+} da_status;
+
+/* Library ABI version (major * 100 + minor). */
+int da_version(void);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *da_status_string(da_status status);
+
+/*
+ * Work partition ("split-KV"): the cache rows of all sequences are cut into
+ * tiles and the flat list of tiles is divided evenly among `num_workers`
+ * workers; a sequence touched by several workers is merged afterwards by a
+ * log-sum-exp combine. num_workers = 0 lets the library choose from the
+ * device's compute-unit count and the shapes. Any value >= 1 is valid and
+ * gives the same result up to fp32 rounding.
+ */
+
+/*
+ * Bytes of workspace mla_decode needs for these shapes and num_workers (same
+ * meaning as in mla_decode). Returns 0 for arguments mla_decode would reject.
+ */
+size_t mla_decode_workspace_size(int b, int s, int h, int k, int p, int t_max, int num_workers);
+
+/*
+ * Absorbed-latent MLA decode.
+ *   q_lat   [b, s, h, k]     bf16   absorbed queries, row (b, i, head)
+ *   q_rope  [b, s, h, p]     bf16   rope part of the queries
+ *   cache   [b, t_max, k+p]  bf16   per token: k latent columns, then p rope columns
+ *   seqlens [b]              int32  valid cache rows per sequence, drafts included
+ *   scale                    fp32   multiplies the full latent+rope dot product
+ *   out_lat [b, s, h, k]     bf16   softmax-weighted latent rows (value = latent part)
+ *   lse     [b, s, h]        fp32   natural-log log-sum-exp of the scaled scores
+ *   workspace                device memory of at least
+ *                            mla_decode_workspace_size(b, s, h, k, p, t_max, num_workers)
+ *                            bytes, 256-byte aligned; its contents on entry do not matter.
+ * Compiled set: (k, p) in {(512, 64), (256, 64), (128, 64), (64, 16)}, h >= 1,
+ * s * h <= 65536.
+ */
+da_status mla_decode(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *cache,
+                     const int32_t *seqlens, int b, int s, int h, int k, int p, int t_max,
+                     float scale, uint16_t *out_lat, float *lse, void *workspace,
+                     size_t workspace_bytes, int num_workers, void *stream);
+
+/* Bytes of workspace gqa_decode needs (0 for arguments gqa_decode would reject). */
+size_t gqa_decode_workspace_size(int b, int s, int hq, int hkv, int d, int t_max, int num_workers);
+
+/*
+ * Grouped-query decode (MHA when hkv == hq, MQA when hkv == 1).
+ *   q       [b, s, hq, d]      bf16
+ *   k_cache [b, t_max, hkv, d] bf16
+ *   v_cache [b, t_max, hkv, d] bf16
+ *   seqlens [b]                int32
+ *   out     [b, s, hq, d]      bf16
+ *   lse     [b, s, hq]         fp32 (natural log)
+ * Query head hh reads K/V head hh / (hq / hkv).
+ * Compiled set: d in {64, 128, 256}; (hq / hkv) * s <= 64.
+ * `path`: 0 = automatic (VALU dot kernel when (hq/hkv)*s < 16, MFMA kernel
+ * otherwise), 1 = force the VALU kernel (needs (hq/hkv)*s <= 16),
+ * 2 = force the MFMA kernel.
+ */
+da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                     const int32_t *seqlens, int b, int s, int hq, int hkv, int d, int t_max,
+                     float scale, uint16_t *out, float *lse, void *workspace,
+                     size_t workspace_bytes, int num_workers, int path, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H */

@@ -1,0 +1,222 @@
+"""GPU parity: the HIP library through its C ABI against the fp64 oracle.
+
+Bar (floating point): max |out - out_ref| <= 1e-2 * max |out_ref| over the
+compared rows, and |lse - lse_ref| <= 1e-3 on rows that see at least one
+cache row; rows that see none must be exactly out = 0, lse = -inf.
+Small shapes are compared on every output; the full-size workloads on a
+seeded sample of rows, in the launch configuration the benchmark times.
+The workspace is poisoned (0xFF bytes = NaN) before every call so that a read
+of an unwritten partial shows up.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def da():
+    dev()
+    import decode_attention_bf16_amd as pkg
+    from decode_attention_bf16_amd import binding
+    binding.load_library()
+    return binding
+
+
+def poisoned(nbytes, device):
+    return torch.full((max(nbytes, 256),), 0xFF, dtype=torch.uint8, device=device)
+
+
+def compare(out_gpu, lse_gpu, out_ref, lse_ref, what=""):
+    o = out_gpu.detach().float().cpu().numpy().astype(np.float64).reshape(out_ref.shape)
+    l = lse_gpu.detach().cpu().numpy().astype(np.float64).reshape(lse_ref.shape)
+    empty = np.isneginf(lse_ref)
+    assert np.all(np.isneginf(l[empty])), what + ": rows with no visible cache row must have lse=-inf"
+    assert np.all(o[empty] == 0), what + ": rows with no visible cache row must be 0"
+    full = ~empty
+    if full.any():
+        ref_max = np.abs(out_ref[full]).max()
+        err = np.abs(o[full] - out_ref[full]).max()
+        assert np.isfinite(o[full]).all(), what + ": non-finite output"
+        assert err <= OUT_TOL * ref_max, "%s: max|dout| %.3e > %.1e * %.3e" % (what, err, OUT_TOL, ref_max)
+        lerr = np.abs(l[full] - lse_ref[full]).max()
+        assert lerr <= LSE_TOL, "%s: max|dlse| %.3e" % (what, lerr)
+
+
+def run_mla(da, shape, tensors, num_workers=0, rows=None, oracle_mod=None):
+    ql, qr, c, sl = tensors
+    d = dev()
+    g = [t.to(d) for t in (ql, qr, c, sl)]
+    nbytes = da.mla_decode_workspace_size(shape.b, shape.s, shape.h, shape.k, shape.p, shape.t_max, num_workers)
+    ws = poisoned(nbytes, d)
+    out, lse = da.mla_decode(*g, shape.scale, num_workers=num_workers, workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def mla_shape(b, s, h, k, p, t, seed, seqlens=None, scale=None):
+    return wl.MLAShape(b=b, s=s, h=h, k=k, p=p, t_max=t, scale=scale or 1.0 / math.sqrt(192), seed=seed)
+
+
+# ------------------------------------------------------------------ MLA, small shapes, full compare
+@pytest.mark.parametrize("workers", [0, 1, 2, 7])
+def test_mla_tiny_workload(da, oracle_mod, workers):
+    shape = wl.MLA_TINY
+    t = wl.make_mla(shape)
+    out, lse = run_mla(da, shape, t, workers)
+    ref_o, ref_l = oracle_mod.mla(*t, shape.scale)
+    print("mla tiny workers=%d" % workers, flush=True)
+    compare(out, lse, ref_o, ref_l, "mla_tiny w=%d" % workers)
+
+
+MLA_SMALL = [
+    # (b, s, h, k, p, t_max, seqlens)
+    (2, 1, 128, 512, 64, 200, [200, 77]),        # partial last tile, two row blocks
+    (3, 3, 20, 512, 64, 150, [150, 64, 2]),      # drafts; row block partly empty; L < s
+    (2, 4, 16, 256, 64, 130, [129, 130]),
+    (1, 2, 40, 128, 64, 96, [95]),
+    (4, 1, 16, 64, 16, 300, [0, 1, 300, 9999]),  # empty and clamped sequences
+    (2, 1, 128, 512, 64, 64, [64, 63]),          # exactly one tile
+]
+
+
+@pytest.mark.parametrize("case", MLA_SMALL, ids=lambda c: "b%d_s%d_h%d_k%d_t%d" % (c[0], c[1], c[2], c[3], c[5]))
+@pytest.mark.parametrize("workers", [0, 1, 3])
+def test_mla_small(da, oracle_mod, case, workers):
+    b, s, h, k, p, t, sl = case
+    shape = mla_shape(b, s, h, k, p, t, seed=100 + b + s + h)
+    tensors = wl.make_mla(shape, seqlens=sl)
+    print("mla small", case, "workers", workers, flush=True)
+    out, lse = run_mla(da, shape, tensors, workers)
+    ref_o, ref_l = oracle_mod.mla(*tensors, shape.scale)
+    compare(out, lse, ref_o, ref_l, "mla %s w=%d" % (case, workers))
+
+
+def test_mla_split_counts_agree(da):
+    shape = mla_shape(4, 2, 64, 512, 64, 700, seed=7)
+    tensors = wl.make_mla(shape, seqlens=[700, 511, 65, 300])
+    res = [run_mla(da, shape, tensors, w) for w in (1, 2, 7, 0, 40)]
+    base_o, base_l = res[0]
+    for o, l in res[1:]:
+        assert (o.float() - base_o.float()).abs().max().item() <= 2 ** -7 * base_o.float().abs().max().item()
+        fin = torch.isfinite(base_l)
+        assert torch.equal(torch.isfinite(l), fin)
+        assert (l[fin] - base_l[fin]).abs().max().item() <= 1e-4
+
+
+def test_mla_cache_row_permutation(da):
+    shape = mla_shape(1, 1, 64, 512, 64, 320, seed=8)
+    ql, qr, c, sl = wl.make_mla(shape, seqlens=[300])
+    o1, l1 = run_mla(da, shape, (ql, qr, c, sl))
+    perm = torch.randperm(300, generator=torch.Generator().manual_seed(3))
+    c2 = c.clone()
+    c2[0, :300] = c[0, perm]
+    o2, l2 = run_mla(da, shape, (ql, qr, c2, sl))
+    assert (o1.float() - o2.float()).abs().max().item() <= 2 ** -7 * o1.float().abs().max().item()
+    assert (l1 - l2).abs().max().item() <= 1e-4
+
+
+def test_mla_garbage_beyond_seqlen_is_ignored(da, oracle_mod):
+    """Cache rows past a sequence's length may hold anything (here NaN/Inf)."""
+    shape = mla_shape(2, 2, 32, 512, 64, 256, seed=9)
+    ql, qr, c, sl = wl.make_mla(shape, seqlens=[100, 37])
+    ref_o, ref_l = oracle_mod.mla(ql, qr, c, sl, shape.scale)
+    c[0, 100:] = float("nan")
+    c[1, 37:] = float("inf")
+    out, lse = run_mla(da, shape, (ql, qr, c, sl))
+    compare(out, lse, ref_o, ref_l, "garbage rows")
+
+
+# ------------------------------------------------------------------ MLA, full-size workloads, sampled rows
+def full_size_mla(da, oracle_mod, shape, n_rows=192):
+    tensors = wl.make_mla(shape)
+    print("full-size mla b=%d s=%d t_max=%d" % (shape.b, shape.s, shape.t_max), flush=True)
+    out, lse = run_mla(da, shape, tensors, 0)
+    rows = wl.sample_rows(shape.rows, n_rows, shape.seed).numpy()
+    ref_o, ref_l = oracle_mod.mla(*tensors, shape.scale, rows=rows)
+    compare(out.reshape(-1, shape.k)[rows], lse.reshape(-1)[rows], ref_o, ref_l, "full mla s=%d" % shape.s)
+    assert torch.isfinite(lse).all() or shape.ragged is not None
+    return tensors, out, lse
+
+
+def test_mla_dsv3_full_size(da, oracle_mod):
+    full_size_mla(da, oracle_mod, wl.MLA_DSV3)
+
+
+def test_mla_mtp4_full_size(da, oracle_mod):
+    full_size_mla(da, oracle_mod, wl.MLA_MTP4)
+
+
+def test_mla_ragged_full_size(da, oracle_mod):
+    full_size_mla(da, oracle_mod, wl.MLA_RAGGED, n_rows=96)
+
+
+# ------------------------------------------------------------------ GQA
+def run_gqa(da, shape, tensors, num_workers=0, path=0):
+    q, k, v, sl = tensors
+    d = dev()
+    g = [t.to(d) for t in (q, k, v, sl)]
+    nbytes = da.gqa_decode_workspace_size(shape.b, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max, num_workers)
+    ws = poisoned(nbytes, d)
+    out, lse = da.gqa_decode(*g, shape.scale, num_workers=num_workers, path=path, workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+GQA_SMALL = [
+    # (b, s, hq, hkv, d, t_max, seqlens)
+    (2, 1, 8, 8, 128, 200, [200, 77]),      # MHA
+    (2, 1, 8, 1, 128, 130, [130, 5]),       # MQA
+    (3, 2, 16, 4, 64, 150, [150, 64, 1]),   # groups of 4, drafts, L < s
+    (2, 1, 32, 4, 256, 96, [96, 33]),       # d = 256, group 8
+    (2, 2, 16, 2, 128, 300, [0, 299]),      # group 8 x 2 drafts = 16 rows, empty sequence
+    (1, 1, 6, 3, 128, 70, [70]),            # group 2
+]
+
+
+@pytest.mark.parametrize("case", GQA_SMALL, ids=lambda c: "b%d_s%d_hq%d_hkv%d_d%d" % c[:5])
+@pytest.mark.parametrize("workers", [0, 1, 5])
+def test_gqa_small(da, oracle_mod, case, workers):
+    b, s, hq, hkv, d, t, sl = case
+    shape = wl.GQAShape(b=b, s=s, hq=hq, hkv=hkv, d=d, t_max=t, scale=1.0 / math.sqrt(d), seed=200 + hq + d)
+    tensors = wl.make_gqa(shape, seqlens=sl)
+    print("gqa small", case, "workers", workers, flush=True)
+    out, lse = run_gqa(da, shape, tensors, workers)
+    ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale)
+    compare(out, lse, ref_o, ref_l, "gqa %s w=%d" % (case, workers))
+
+
+def test_gqa_layer_full_size(da, oracle_mod):
+    shape = wl.GQA_LAYER
+    tensors = wl.make_gqa(shape)
+    print("full-size gqa", flush=True)
+    out, lse = run_gqa(da, shape, tensors, 0)
+    rows = wl.sample_rows(shape.rows, 512, shape.seed).numpy()
+    ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale, rows=rows)
+    compare(out.reshape(-1, shape.d)[rows], lse.reshape(-1)[rows], ref_o, ref_l, "gqa full")
+
+
+def test_gqa_mha_equals_repeated_kv(da):
+    """GQA equals MHA run on K/V heads repeated per group (GPU against GPU)."""
+    shape = wl.GQAShape(b=2, s=1, hq=16, hkv=2, d=128, t_max=256, scale=1.0 / math.sqrt(128), seed=5)
+    q, k, v, sl = wl.make_gqa(shape, seqlens=[256, 100])
+    o1, l1 = run_gqa(da, shape, (q, k, v, sl))
+    mha = wl.GQAShape(b=2, s=1, hq=16, hkv=16, d=128, t_max=256, scale=shape.scale, seed=5)
+    o2, l2 = run_gqa(da, mha, (q, k.repeat_interleave(8, dim=2).contiguous(),
+                               v.repeat_interleave(8, dim=2).contiguous(), sl))
+    assert (o1.float() - o2.float()).abs().max().item() <= 2 ** -7 * o1.float().abs().max().item()
+    assert (l1 - l2).abs().max().item() <= 1e-4
