@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+One step = one pass of the whole hot path over the b=32, t=4096 decode
+workloads: grouped-query decode (64 query / 8 KV heads, d=128, s=1), absorbed
+MLA decode (h=128, k=512, p=64) at s=1, and at s=4 draft tokens. Each call runs
+the device planner, the tile kernel and the log-sum-exp combine. Inputs are
+seeded synthetic bf16 N(0,1) tensors, resident in HBM before timing; the three
+workloads together stream ~840 MB per step, so no input stays in the 256 MB
+last-level cache between its uses.
+
+Prints ONE JSON line: value = algorithmic TFLOP/s of the step (closed-form
+FLOPs / wall time per step), plus per-part kernel times from HIP events, the
+roofline placement of the dominant call and the fp64 CPU oracle timed on a
+sample of the same rows.
+
+    python bench.py [--steps K] [--warmup W] [--cpu-sample F] [--no-cpu]
+    python bench.py --sweep          # s-sweep of MLA (one JSON line per s, for the ridge crossing)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import workloads as wl  # noqa: E402
+from decode_attention_bf16_amd import binding  # noqa: E402
+from decode_attention_bf16_amd import costmodel as cm  # noqa: E402
+
+PEAK_TFLOPS = cm.MI355X_BF16_FLOPS / 1e12
+PEAK_GBS = cm.MI355X_HBM_BYTES_PER_S / 1e9
+RIDGE = cm.MI355X_BF16_FLOPS / cm.MI355X_HBM_BYTES_PER_S
+CSRC = os.path.join(ROOT, "decode_attention_bf16_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+class Part:
+    """One decode call of the step, with preallocated outputs and workspace."""
+
+    def __init__(self, name, kind, shape, dev):
+        self.name, self.kind, self.shape = name, kind, shape
+        if kind == "mla":
+            cpu = wl.make_mla(shape)
+            self.cost = cm.mla_absorbed(shape.b, shape.h, shape.s, shape.t_max, shape.k, shape.p)
+            self.flops_masked = cm.mla_absorbed_ragged(cpu[3].tolist(), shape.h, shape.s, shape.k, shape.p,
+                                                       shape.t_max, masked=True).flops
+            nbytes = binding.mla_decode_workspace_size(shape.b, shape.s, shape.h, shape.k, shape.p, shape.t_max)
+            self.out = torch.empty((shape.b, shape.s, shape.h, shape.k), dtype=torch.bfloat16, device=dev)
+            self.lse = torch.empty((shape.b, shape.s, shape.h), dtype=torch.float32, device=dev)
+        else:
+            cpu = wl.make_gqa(shape)
+            self.cost = cm.gqa(shape.b, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max)
+            self.flops_masked = cm.gqa_ragged(cpu[3].tolist(), shape.s, shape.hq, shape.hkv, shape.d, shape.t_max,
+                                              masked=True).flops
+            nbytes = binding.gqa_decode_workspace_size(shape.b, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max)
+            self.out = torch.empty((shape.b, shape.s, shape.hq, shape.d), dtype=torch.bfloat16, device=dev)
+            self.lse = torch.empty((shape.b, shape.s, shape.hq), dtype=torch.float32, device=dev)
+        self.cpu = cpu
+        self.gpu = [t.to(dev) for t in cpu]
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.bound = "mfma" if self.cost.ai > RIDGE else "hbm"
+        self.t_min = cm.roofline_time(self.cost)
+
+    def __call__(self):
+        if self.kind == "mla":
+            binding.mla_decode(*self.gpu, self.shape.scale, out=self.out, lse=self.lse, workspace=self.ws)
+        else:
+            binding.gqa_decode(*self.gpu, self.shape.scale, out=self.out, lse=self.lse, workspace=self.ws)
+
+    def roofline(self, sec):
+        if self.bound == "mfma":
+            a = self.cost.flops / sec / 1e12
+            return {"bound": "mfma", "achieved": round(a, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(a / PEAK_TFLOPS, 4)}
+        a = self.cost.bytes / sec / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(a / PEAK_GBS, 4)}
+
+
+def time_parts(parts, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for p in parts:
+            p()
+    torch.cuda.synchronize()
+    evs = {p.name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in range(steps)] for p in parts}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        for p in parts:
+            a, b = evs[p.name][k]
+            a.record(stream)
+            p()
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    per = {p.name: sum(a.elapsed_time(b) for a, b in evs[p.name]) / steps / 1e3 for p in parts}
+    return wall, per
+
+
+def cpu_baseline(parts, fraction):
+    import oracle
+    oracle.build(force=False)
+    tot_flops = 0.0
+    t0 = time.perf_counter()
+    for p in parts:
+        n = max(1, int(p.shape.rows * fraction))
+        rows = wl.sample_rows(p.shape.rows, n, p.shape.seed).numpy()
+        if p.kind == "mla":
+            _, _, macs = oracle.mla(*p.cpu, p.shape.scale, rows=rows, return_macs=True)
+        else:
+            _, _, macs = oracle.gqa(*p.cpu, p.shape.scale, rows=rows, return_macs=True)
+        tot_flops += 2.0 * macs
+    dt = time.perf_counter() - t0
+    return {"value": round(tot_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "fp64 oracle on a seeded %.0f%% sample of the query rows of each of the step's three "
+                      "workloads (%.1f GFLOP, %.1f s)" % (100 * fraction, tot_flops / 1e9, dt)}
+
+
+def load_traffic(name):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(name)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_call")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-sample", type=float, default=0.5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of parts to run (gqa,mla_s1,mla_s4)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (the decode kernels shard by "
+              "batch or KV head with no communication; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    binding.load_library()
+
+    if args.sweep:
+        for s in wl.MTP_SWEEP:
+            p = Part("mla_s%d" % s, "mla", wl.mla_mtp(s), dev)
+            wall, per = time_parts([p], args.steps, args.warmup)
+            sec = per[p.name]
+            print(json.dumps({"sweep": "mla_mtp", "s": s, "us": round(sec * 1e6, 2),
+                              "tflops": round(p.cost.flops / sec / 1e12, 2),
+                              "tbs": round(p.cost.bytes / sec / 1e12, 3), "ai": round(p.cost.ai, 1),
+                              "bound": p.bound, "t_min_us": round(p.t_min * 1e6, 2),
+                              "roofline_frac": round(p.t_min / sec, 4)}), flush=True)
+            del p
+            torch.cuda.empty_cache()
+        return
+
+    parts = [Part("gqa", "gqa", wl.GQA_LAYER, dev), Part("mla_s1", "mla", wl.MLA_DSV3, dev),
+             Part("mla_s4", "mla", wl.MLA_MTP4, dev)]
+    if args.only:
+        keep = set(args.only.split(","))
+        parts = [p for p in parts if p.name in keep]
+    wall, per = time_parts(parts, args.steps, args.warmup)
+
+    flops = sum(p.cost.flops for p in parts)
+    byts = sum(p.cost.bytes for p in parts)
+    dom = max(parts, key=lambda p: per[p.name])
+    roof = dom.roofline(per[dom.name])
+    traffic = load_traffic(dom.name)
+    roof["traffic"] = traffic
+    roof["kernel"] = dom.name
+    part_info = {}
+    for p in parts:
+        sec = per[p.name]
+        part_info[p.name] = {"us": round(sec * 1e6, 2), "tflops": round(p.cost.flops / sec / 1e12, 2),
+                             "tbs": round(p.cost.bytes / sec / 1e12, 3), "ai": round(p.cost.ai, 1),
+                             "bound": p.bound, "t_min_us": round(p.t_min * 1e6, 2),
+                             "roofline_frac": round(p.t_min / sec, 4),
+                             "masked_tflops": round(p.flops_masked / sec / 1e12, 2)}
+    res = {
+        "metric": "decode-attn TFLOP/s + HBM TB/s (% of MI355X roofline), b=32 t=4096, s=1 and s=4",
+        "value": round(flops / wall / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "+".join(p.name for p in parts) + " (b=32, t=4096: gqa hq=64 hkv=8 d=128 s=1; "
+                               "mla h=128 k=512 p=64 s=1 and s=4)",
+                   "global_batch": 32, "seq_len": 4096, "parallelism": "single-gpu"},
+        "hbm_tbs": round(byts / wall / 1e12, 3),
+        "step_roofline_frac": round(sum(p.t_min for p in parts) / wall, 4),
+        "roofline": roof,
+        "parts": part_info,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(parts, args.cpu_sample)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

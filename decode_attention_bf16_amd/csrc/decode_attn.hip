@@ -101,7 +101,7 @@ hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint1
     if (log_plan())
         fprintf(stderr, "[decode_attn] mla k=%d p=%d b=%d s=%d h=%d t_max=%d workers=%d row_blocks=%d grid=%d lds=%d\n",
                 K, P, b, s, h, t_max, workers, rb, grid, C::LDS_BYTES);
-    hipLaunchKernelGGL((da::mla_decode_kernel<K, P>), dim3(grid), dim3(256), C::LDS_BYTES, stream, q_lat, q_rope,
+    hipLaunchKernelGGL((da::mla_decode_kernel<K, P>), dim3(grid), dim3(C::THREADS), C::LDS_BYTES, stream, q_lat, q_rope,
                        cache, seqlens, b, s, h, t_max, scale_log2, rb, units, hdr, tile_start, slot_start, out, lse,
                        part_out, part_lse);
     const long rows = (long)b * s * h;

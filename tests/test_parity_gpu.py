@@ -91,6 +91,9 @@ MLA_SMALL = [
     (1, 2, 40, 128, 64, 96, [95]),
     (4, 1, 16, 64, 16, 300, [0, 1, 300, 9999]),  # empty and clamped sequences
     (2, 1, 128, 512, 64, 64, [64, 63]),          # exactly one tile
+    (4, 1, 16, 512, 64, 300, [0, 1, 300, 9999]),  # one row group with rows, workers spanning sequences
+    (2, 1, 16, 128, 64, 300, [65, 300]),
+    (2, 2, 24, 512, 64, 300, [300, 1]),            # the repair round needed by some row groups only
 ]
 
 
