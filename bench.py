@@ -53,8 +53,8 @@ def kernel_source_hash() -> str:
 class Part:
     """One decode call of the step, with preallocated outputs and workspace."""
 
-    def __init__(self, name, kind, shape, dev):
-        self.name, self.kind, self.shape = name, kind, shape
+    def __init__(self, name, kind, shape, dev, path=0):
+        self.name, self.kind, self.shape, self.path = name, kind, shape, path
         if kind == "mla":
             cpu = wl.make_mla(shape)
             self.cost = cm.mla_absorbed(shape.b, shape.h, shape.s, shape.t_max, shape.k, shape.p)
@@ -68,7 +68,8 @@ class Part:
             self.cost = cm.gqa(shape.b, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max)
             self.flops_masked = cm.gqa_ragged(cpu[3].tolist(), shape.s, shape.hq, shape.hkv, shape.d, shape.t_max,
                                               masked=True).flops
-            nbytes = binding.gqa_decode_workspace_size(shape.b, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max)
+            nbytes = binding.gqa_decode_workspace_size(shape.b, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max, 0,
+                                                       self.path)
             self.out = torch.empty((shape.b, shape.s, shape.hq, shape.d), dtype=torch.bfloat16, device=dev)
             self.lse = torch.empty((shape.b, shape.s, shape.hq), dtype=torch.float32, device=dev)
         self.cpu = cpu
@@ -81,7 +82,8 @@ class Part:
         if self.kind == "mla":
             binding.mla_decode(*self.gpu, self.shape.scale, out=self.out, lse=self.lse, workspace=self.ws)
         else:
-            binding.gqa_decode(*self.gpu, self.shape.scale, out=self.out, lse=self.lse, workspace=self.ws)
+            binding.gqa_decode(*self.gpu, self.shape.scale, path=self.path, out=self.out, lse=self.lse,
+                               workspace=self.ws)
 
     def roofline(self, sec):
         if self.bound == "mfma":
@@ -155,6 +157,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--only", default="", help="comma list of parts to run (gqa,mla_s1,mla_s4)")
+    ap.add_argument("--gqa-path", type=int, default=0, help="GQA kernel: 0 auto, 1 VALU dot, 2 MFMA")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB a few times (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -165,6 +170,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
     binding.load_library()
 
     if args.sweep:
@@ -181,7 +195,7 @@ def main():
             torch.cuda.empty_cache()
         return
 
-    parts = [Part("gqa", "gqa", wl.GQA_LAYER, dev), Part("mla_s1", "mla", wl.MLA_DSV3, dev),
+    parts = [Part("gqa", "gqa", wl.GQA_LAYER, dev, args.gqa_path), Part("mla_s1", "mla", wl.MLA_DSV3, dev),
              Part("mla_s4", "mla", wl.MLA_MTP4, dev)]
     if args.only:
         keep = set(args.only.split(","))

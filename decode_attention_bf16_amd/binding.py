@@ -54,7 +54,7 @@ def load_library():
         lib.mla_decode_workspace_size.restype = Z
         lib.mla_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, P]
         lib.mla_decode.restype = I
-        lib.gqa_decode_workspace_size.argtypes = [I] * 7
+        lib.gqa_decode_workspace_size.argtypes = [I] * 8
         lib.gqa_decode_workspace_size.restype = Z
         lib.gqa_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, I, P]
         lib.gqa_decode.restype = I
@@ -95,8 +95,8 @@ def mla_decode_workspace_size(b, s, h, k, p, t_max, num_workers=0) -> int:
     return int(load_library().mla_decode_workspace_size(b, s, h, k, p, t_max, num_workers))
 
 
-def gqa_decode_workspace_size(b, s, hq, hkv, d, t_max, num_workers=0) -> int:
-    return int(load_library().gqa_decode_workspace_size(b, s, hq, hkv, d, t_max, num_workers))
+def gqa_decode_workspace_size(b, s, hq, hkv, d, t_max, num_workers=0, path=0) -> int:
+    return int(load_library().gqa_decode_workspace_size(b, s, hq, hkv, d, t_max, num_workers, path))
 
 
 def _workspace(nbytes, device, workspace):
@@ -173,7 +173,7 @@ def gqa_decode(q, k_cache, v_cache, seqlens, scale, num_workers=0, path=0, out=N
         lse = torch.empty((b, s, hq), dtype=torch.float32, device=dev)
     else:
         _need(lse, "lse", torch.float32, 3, dev)
-    nbytes = lib.gqa_decode_workspace_size(b, s, hq, hkv, d, t_max, num_workers)
+    nbytes = lib.gqa_decode_workspace_size(b, s, hq, hkv, d, t_max, num_workers, path)
     ws = _workspace(nbytes, dev, workspace)
     with torch.cuda.device(dev):
         rc = lib.gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), b, s, hq, hkv, d, t_max,

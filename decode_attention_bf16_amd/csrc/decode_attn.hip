@@ -112,11 +112,18 @@ hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint1
 
 // ------------------------------------------------------------------ GQA
 int gqa_head_blocks(int hkv) { return (hkv + 3) / 4; }
+int gqa_choose_path(int rows, int path);
 
-int gqa_workers(int b, int hkv, int t_max, int requested)
+int gqa_workers(int b, int hkv, int d, int rows, int path, int t_max, int requested)
 {
     if (requested > 0) return requested;
-    int w = 2 * current_cu_count() / gqa_head_blocks(hkv);
+    int w;
+    if (gqa_choose_path(rows, path) == 0) {
+        w = 2 * current_cu_count() / gqa_head_blocks(hkv);
+    } else {
+        const int hpb = 512 / d;  // heads per MFMA block; one block per CU (LDS ring)
+        w = current_cu_count() / ((hkv + hpb - 1) / hpb);
+    }
     if (w < 1) w = 1;
     const long max_tiles = (long)b * ((t_max + da::kGqaTile - 1) / da::kGqaTile);
     if ((long)w > max_tiles) w = (int)max_tiles;
@@ -159,6 +166,53 @@ bool dispatch_gqa_valu(int rows, const uint16_t *q, const uint16_t *k, const uin
     return false;
 }
 
+template <int D, int RBLK>
+hipError_t launch_gqa_mfma(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *seqlens, int b,
+                           int s, int hq, int hkv, int t_max, float scale_log2, uint16_t *out, float *lse,
+                           da::PlanHeader *hdr, int *tile_start, int *slot_start, float *part_out, float *part_lse,
+                           int workers, hipStream_t stream)
+{
+    using C = da::GqaMfmaCfg<D, RBLK>;
+    static std::once_flag attr_once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(attr_once, [] {
+        attr_err = hipFuncSetAttribute((const void *)da::gqa_mfma_kernel<D, RBLK>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    const int hb = (hkv + C::HPB - 1) / C::HPB;
+    const int units = workers * hb;
+    const int grid = (units + 7) / 8 * 8;
+    hipLaunchKernelGGL((da::gqa_mfma_kernel<D, RBLK>), dim3(grid), dim3(C::THREADS), C::LDS_BYTES, stream, q, k, v,
+                       seqlens, b, s, hq, hkv, t_max, scale_log2, hb, units, hdr, tile_start, slot_start, out, lse,
+                       part_out, part_lse);
+    return hipSuccess;
+}
+
+template <int D>
+hipError_t dispatch_gqa_mfma(int rows, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const int32_t *seqlens, int b, int s, int hq, int hkv, int t_max, float scale_log2,
+                             uint16_t *out, float *lse, da::PlanHeader *hdr, int *tile_start, int *slot_start,
+                             float *part_out, float *part_lse, int workers, hipStream_t stream)
+{
+    if (rows <= 16)
+        return launch_gqa_mfma<D, 1>(q, k, v, seqlens, b, s, hq, hkv, t_max, scale_log2, out, lse, hdr, tile_start,
+                                     slot_start, part_out, part_lse, workers, stream);
+    if (rows <= 32 || D == 256)
+        return launch_gqa_mfma<D, 2>(q, k, v, seqlens, b, s, hq, hkv, t_max, scale_log2, out, lse, hdr, tile_start,
+                                     slot_start, part_out, part_lse, workers, stream);
+    return launch_gqa_mfma<D, (D == 256 ? 2 : 4)>(q, k, v, seqlens, b, s, hq, hkv, t_max, scale_log2, out, lse, hdr,
+                                                  tile_start, slot_start, part_out, part_lse, workers, stream);
+}
+
+// 0 = VALU dot kernel, 1 = MFMA kernel
+int gqa_choose_path(int rows, int path)
+{
+    if (path == 1) return 0;
+    if (path == 2) return 1;
+    return rows < 16 ? 0 : 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,6 +242,8 @@ static da_status mla_check(int b, int s, int h, int k, int p, int t_max, int num
     if (s > t_max) return DA_ERR_INVALID_ARG;
     if (!mla_supported(k, p)) return DA_ERR_UNSUPPORTED;
     if ((long)s * h > 65536) return DA_ERR_UNSUPPORTED;
+    // one sequence's cache rows must be addressable by a 32-bit buffer offset
+    if ((long long)t_max * (k + p) * 2 >= (1LL << 31)) return DA_ERR_UNSUPPORTED;
     return DA_OK;
 }
 
@@ -228,19 +284,24 @@ da_status mla_decode(const uint16_t *q_lat, const uint16_t *q_rope, const uint16
     return e == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 
-static da_status gqa_check(int b, int s, int hq, int hkv, int d, int t_max, int num_workers)
+static da_status gqa_check(int b, int s, int hq, int hkv, int d, int t_max, int num_workers, int path)
 {
     if (b <= 0 || s <= 0 || hq <= 0 || hkv <= 0 || d <= 0 || t_max <= 0 || num_workers < 0) return DA_ERR_INVALID_ARG;
     if (hq % hkv != 0 || s > t_max) return DA_ERR_INVALID_ARG;
+    if (path < 0 || path > 2) return DA_ERR_INVALID_ARG;
     if (!(d == 64 || d == 128 || d == 256)) return DA_ERR_UNSUPPORTED;
-    if ((hq / hkv) * s > 16) return DA_ERR_UNSUPPORTED;
+    const int rows = (hq / hkv) * s;
+    if (rows > (d == 256 ? 32 : 64)) return DA_ERR_UNSUPPORTED;
+    if (gqa_choose_path(rows, path) == 0 && !gqa_valu_ok(rows)) return DA_ERR_UNSUPPORTED;
+    // one sequence's K (or V) rows must be addressable by a 32-bit buffer offset
+    if ((long long)t_max * hkv * d * 2 >= (1LL << 31)) return DA_ERR_UNSUPPORTED;
     return DA_OK;
 }
 
-size_t gqa_decode_workspace_size(int b, int s, int hq, int hkv, int d, int t_max, int num_workers)
+size_t gqa_decode_workspace_size(int b, int s, int hq, int hkv, int d, int t_max, int num_workers, int path)
 {
-    if (gqa_check(b, s, hq, hkv, d, t_max, num_workers) != DA_OK) return 0;
-    const int w = gqa_workers(b, hkv, t_max, num_workers);
+    if (gqa_check(b, s, hq, hkv, d, t_max, num_workers, path) != DA_OK) return 0;
+    const int w = gqa_workers(b, hkv, d, (hq / hkv) * s, path, t_max, num_workers);
     return da::ws_layout(b, s * hq, d, w).total;
 }
 
@@ -248,17 +309,15 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
                      int b, int s, int hq, int hkv, int d, int t_max, float scale, uint16_t *out, float *lse,
                      void *workspace, size_t workspace_bytes, int num_workers, int path, void *stream)
 {
-    da_status st = gqa_check(b, s, hq, hkv, d, t_max, num_workers);
+    da_status st = gqa_check(b, s, hq, hkv, d, t_max, num_workers, path);
     if (st != DA_OK) return st;
-    if (path < 0 || path > 2) return DA_ERR_INVALID_ARG;
-    if (path == 2) return DA_ERR_UNSUPPORTED;
     if (!q || !k_cache || !v_cache || !seqlens || !out || !lse || !workspace) return DA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return DA_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255u) != 0) return DA_ERR_INVALID_ARG;
     if (!std::isfinite(scale) || !(scale > 0.f)) return DA_ERR_INVALID_ARG;
     const int rows = (hq / hkv) * s;
-    if (!gqa_valu_ok(rows)) return DA_ERR_UNSUPPORTED;
-    const int workers = gqa_workers(b, hkv, t_max, num_workers);
+    const int use_mfma = gqa_choose_path(rows, path);
+    const int workers = gqa_workers(b, hkv, d, rows, path, t_max, num_workers);
     const da::WsLayout ws = da::ws_layout(b, s * hq, d, workers);
     if (workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
 
@@ -274,10 +333,23 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
     hipLaunchKernelGGL(da::plan_kernel, dim3(1), dim3(da::kPlanThreads), 0, st_, seqlens, b, t_max, da::kGqaTile,
                        workers, hdr, tile_start, slot_start);
     if (log_plan())
-        fprintf(stderr, "[decode_attn] gqa d=%d b=%d s=%d hq=%d hkv=%d t_max=%d workers=%d path=valu\n", d, b, s, hq,
-                hkv, t_max, workers);
+        fprintf(stderr, "[decode_attn] gqa d=%d b=%d s=%d hq=%d hkv=%d t_max=%d workers=%d path=%s\n", d, b, s, hq,
+                hkv, t_max, workers, use_mfma ? "mfma" : "valu");
     bool ok = false;
-    if (d == 64)
+    if (use_mfma) {
+        hipError_t e;
+        if (d == 64)
+            e = dispatch_gqa_mfma<64>(rows, q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
+                                      tile_start, slot_start, part_out, part_lse, workers, st_);
+        else if (d == 128)
+            e = dispatch_gqa_mfma<128>(rows, q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
+                                       tile_start, slot_start, part_out, part_lse, workers, st_);
+        else
+            e = dispatch_gqa_mfma<256>(rows, q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
+                                       tile_start, slot_start, part_out, part_lse, workers, st_);
+        if (e != hipSuccess) return DA_ERR_HIP;
+        ok = true;
+    } else if (d == 64)
         ok = dispatch_gqa_valu<64>(rows, q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
                                    tile_start, slot_start, part_out, part_lse, workers, st_);
     else if (d == 128)

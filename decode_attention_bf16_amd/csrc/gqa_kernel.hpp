@@ -258,3 +258,264 @@ __global__ void __launch_bounds__(256)
 }
 
 }  // namespace da
+
+namespace da {
+
+// ----------------------------------------------------------------------------
+// MFMA kernel (any R = g*s up to 64, rows padded to blocks of 16).
+//
+// Block = 512/D... waves (one KV head each); the block streams 16-token stages
+// of its heads' K and V rows HBM -> LDS with buffer_load ... lds (a ring of 4
+// stages, 3 in flight while one is computed; rows past the sequence length read
+// as zeros through the buffer bounds). Per wave and stage:
+//   S^T[16 tokens, 16 rows] = K . Q^T   MFMA 16x16x32 bf16, K from LDS, Q in registers
+//   softmax (fp32, exp2 domain, lazily moved per-row reference maximum)
+//   O^T[d, 16 rows] += V^T . P^T        MFMA 16x16x16 bf16, V^T through the LDS
+//                                       transposing read, P^T straight from the
+//                                       score registers
+// LDS stage layout: 16 K token rows then 16 V token rows of 1 KB (the block's
+// heads, d contiguous); 16-byte chunk c of token row t is stored at
+// c ^ gsw(t), gsw(t) = (t & 15) ^ ((t & 1) << 3), which keeps the 16-token score
+// reads and the 4-token transposing reads free of bank conflicts on 64 banks.
+template <int D, int RBLK>
+struct GqaMfmaCfg {
+    static_assert(D == 64 || D == 128 || D == 256, "head dim");
+    static constexpr int HPB = 512 / D;          // KV heads (waves) per block
+    static constexpr int THREADS = 64 * HPB;
+    static constexpr int T = 16;                 // tokens per stage
+    static constexpr int ROWB = 1024;            // bytes of one token row (HPB heads x d)
+    static constexpr int STAGE_BYTES = 2 * T * ROWB;
+    static constexpr int NST = 4;                // ring depth
+    static constexpr int LDS_BYTES = NST * STAGE_BYTES;
+    static constexpr int LW = 2 * T / HPB;       // DMA instructions per wave per stage
+    static constexpr int KS = D / 32;            // score k-steps
+    static constexpr int DB = D / 16;            // 16-wide output blocks
+};
+
+__device__ __forceinline__ int gqa_swz(int t) { return (t & 15) ^ ((t & 1) << 3); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+template <int D, int RBLK>
+__global__ void __launch_bounds__(64 * (512 / D), 1)
+    gqa_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+                    const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens, int B, int s, int hq,
+                    int hkv, int t_max, float scale_log2, int head_blocks, int units,
+                    const PlanHeader *__restrict__ hdr, const int *__restrict__ tile_start,
+                    const int *__restrict__ slot_start, uint16_t *__restrict__ out, float *__restrict__ lse,
+                    float *__restrict__ part_out, float *__restrict__ part_lse)
+{
+    using C = GqaMfmaCfg<D, RBLK>;
+    constexpr int SUB = kGqaTile / C::T;  // stages per planner tile
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    DA_LDS char *lds = (DA_LDS char *)smem;
+
+    const int unit = xcd_linear_unit(blockIdx.x, gridDim.x);
+    if (unit >= units) return;
+    const int worker = unit / head_blocks;
+    const int hb = unit - worker * head_blocks;
+    const int total = hdr->total_tiles;
+    const int per = hdr->per;
+    const int tile_lo = worker * per;
+    if (tile_lo >= total) return;
+    const int tile_hi = min(total, tile_lo + per);
+    const int nst = (tile_hi - tile_lo) * SUB;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int kvh = hb * C::HPB + w;
+    const bool active = kvh < hkv;
+    const int grp = hq / hkv;
+    const int R = grp * s;       // query rows of this KV head
+    const int M = s * hq;        // query rows per sequence
+    const size_t tok_elems = (size_t)hkv * D;
+
+    // ---- per-lane LDS offsets
+    const int qk_base = n * C::ROWB;  // + ((chunk ^ gsw(n)) << 4)
+    const int sq = gqa_swz(n);
+    const int tr_tok = 4 * g + (n >> 2);
+    const int st = gqa_swz(tr_tok);
+    const int hsel = (n & 3) >> 1;
+    const int tr_base = (C::T + tr_tok) * C::ROWB + ((n & 1) << 3);
+
+    // ---- DMA of one stage: rows r = w, w + HPB, ... (0..15 K, 16..31 V)
+    auto stage_pos = [&](int sg, int &bq, int &tok0) {
+        const int tt = tile_lo + sg / SUB;
+        bq = find_sequence(tile_start, B, tt);
+        tok0 = (tt - tile_start[bq]) * kGqaTile + (sg % SUB) * C::T;
+    };
+    auto issue_stage = [&](int sg) {
+        int bq, tok0;
+        stage_pos(sg, bq, tok0);
+        const int L = clamp_len(seqlens[bq], t_max);
+        const int nrec = L * (int)tok_elems * 2;
+        DA_LDS char *dst = lds + (sg % C::NST) * C::STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < C::LW; ++i) {
+            const int r = w + i * C::HPB;  // wave-uniform
+            const int tk = r & 15;
+            const uint16_t *base = (r < 16 ? kc : vc) + (size_t)bq * t_max * tok_elems;
+            __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, nrec, 0x00020000);
+            const int c = lane ^ gqa_swz(tk);
+            const uint32_t off = (uint32_t)(((tok0 + tk) * (int)tok_elems + hb * C::HPB * D) * 2 + c * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (DA_LDS void *)(dst + r * C::ROWB), 16, (int)off, 0, 0, 0);
+        }
+    };
+
+    bf16x8 qB[RBLK][C::KS];
+    f32x4 acc[RBLK][C::DB];
+    float mref[RBLK], lsum[RBLK];
+    int nvis[RBLK];
+    int nvis_min = 0;
+
+    auto row_of = [&](int r) {
+        const int i = r / grp;
+        const int j = r - i * grp;
+        return i * hq + kvh * grp + j;
+    };
+    auto begin_segment = [&](int bq) {
+        const int L = clamp_len(seqlens[bq], t_max);
+        int mn = 0x7fffffff;
+#pragma unroll
+        for (int rb = 0; rb < RBLK; ++rb) {
+            const int r = rb * 16 + n;
+            const bool ok = active && r < R;
+            nvis[rb] = ok ? L - s + r / grp + 1 : 0;
+            mn = min(mn, nvis[rb]);
+#pragma unroll
+            for (int kk = 0; kk < C::KS; ++kk) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (ok) v = *(const u32x4 *)(q + ((size_t)bq * M + row_of(r)) * D + kk * 32 + g * 8);
+                qB[rb][kk] = as_bf16x8(v);
+            }
+            mref[rb] = -INFINITY;
+            lsum[rb] = 0.f;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int off = 1; off < 64; off <<= 1) mn = min(mn, __shfl_xor(mn, off));
+        nvis_min = mn;
+    };
+    auto end_segment = [&](int bq, int first_tile_of_seq) {
+        if (!active) return;
+        const int nseg = slot_start[bq + 1] - slot_start[bq];
+        const int sl = slot_start[bq] + (worker - first_tile_of_seq / per);
+#pragma unroll
+        for (int rb = 0; rb < RBLK; ++rb) {
+            const int r = rb * 16 + n;
+            if (r >= R) continue;
+            const int row = row_of(r);
+            const float inv = lsum[rb] > 0.f ? 1.f / lsum[rb] : 0.f;
+            const float lse2 = lsum[rb] > 0.f ? mref[rb] + fast_log2(lsum[rb]) : -INFINITY;
+            if (nseg == 1) {
+                uint16_t *o = out + ((size_t)bq * M + row) * D + g * 4;
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) {
+                    u32x2 v;
+                    v[0] = pack_bf16x2(acc[rb][db][0] * inv, acc[rb][db][1] * inv);
+                    v[1] = pack_bf16x2(acc[rb][db][2] * inv, acc[rb][db][3] * inv);
+                    *(u32x2 *)(o + db * 16) = v;
+                }
+                if (g == 0) lse[(size_t)bq * M + row] = lse2 * kLn2;
+            } else {
+                float *o = part_out + ((size_t)sl * M + row) * D + g * 4;
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) *(f32x4 *)(o + db * 16) = acc[rb][db] * inv;
+                if (g == 0) part_lse[(size_t)sl * M + row] = lse2;
+            }
+        }
+    };
+
+    // ---- prologue
+    for (int sg = 0; sg < min(3, nst); ++sg) issue_stage(sg);
+    int bcur = find_sequence(tile_start, B, tile_lo);
+    int ts_cur = tile_start[bcur];
+    int te_cur = tile_start[bcur + 1];
+    int L = clamp_len(seqlens[bcur], t_max);
+    begin_segment(bcur);
+
+    for (int sg = 0; sg < nst; ++sg) {
+        const int tt = tile_lo + sg / SUB;
+        if (tt >= te_cur) {  // first stage of a new sequence (stage sg % SUB == 0)
+            end_segment(bcur, ts_cur);
+            bcur = find_sequence(tile_start, B, tt);
+            ts_cur = tile_start[bcur];
+            te_cur = tile_start[bcur + 1];
+            L = clamp_len(seqlens[bcur], t_max);
+            begin_segment(bcur);
+        }
+        // wait for this stage's copies (the later stages issued so far may stay in flight)
+        const int later = min(2, nst - 1 - sg);
+        if (later == 2)
+            wait_vmcnt<2 * C::LW>();
+        else if (later == 1)
+            wait_vmcnt<C::LW>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+        if (sg + 3 < nst) issue_stage(sg + 3);
+
+        const int tok0 = (tt - ts_cur) * kGqaTile + (sg % SUB) * C::T;
+        if (!active || tok0 >= L) continue;
+        const DA_LDS char *stg = lds + (sg % C::NST) * C::STAGE_BYTES;
+
+        // scores
+        f32x4 S[RBLK];
+#pragma unroll
+        for (int rb = 0; rb < RBLK; ++rb) S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk) {
+            const int c = w * (D / 8) + kk * 4 + g;
+            const bf16x8 a = *(const DA_LDS bf16x8 *)(stg + qk_base + ((c ^ sq) << 4));
+#pragma unroll
+            for (int rb = 0; rb < RBLK; ++rb) S[rb] = mfma16x16x32(a, qB[rb][kk], S[rb]);
+        }
+        // mask, online softmax, probabilities
+        i16x4 pB[RBLK];
+#pragma unroll
+        for (int rb = 0; rb < RBLK; ++rb) {
+            if (tok0 + C::T > nvis_min) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (tok0 + g * 4 + i >= nvis[rb]) S[rb][i] = -INFINITY;
+            }
+            float m = fmaxf(fmaxf(S[rb][0], S[rb][1]), fmaxf(S[rb][2], S[rb][3]));
+            const float mt = wave_max_across_groups16(m) * scale_log2;
+            if (__builtin_amdgcn_ballot_w64(mt > mref[rb] + kRescaleSlack)) {
+                const float mnew = fmaxf(mref[rb], mt);
+                const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref[rb] - mnew);
+                mref[rb] = mnew;
+                lsum[rb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) acc[rb][db] *= alpha;
+            }
+            const float ms = mref[rb] == -INFINITY ? 0.f : mref[rb];
+            float p[4], part = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = fast_exp2(__builtin_fmaf(S[rb][i], scale_log2, -ms));
+                part += p[i];
+            }
+            lsum[rb] += wave_sum_across_groups16(part);
+            const u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+            pB[rb] = __builtin_bit_cast(i16x4, pk);
+        }
+        // values
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            const int c = w * (D / 8) + 2 * db + hsel;
+            const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (DA_LDS i16x4 *)(stg + tr_base + ((c ^ st) << 4)));
+#pragma unroll
+            for (int rb = 0; rb < RBLK; ++rb)
+                acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pB[rb], acc[rb][db], 0, 0, 0);
+        }
+    }
+    end_segment(bcur, ts_cur);
+}
+
+}  // namespace da

@@ -36,8 +36,8 @@
 // cache holds there.
 //
 // LDS tile layout: row r (token) holds ROW_CHUNKS 16-byte chunks; logical chunk
-// c is stored at chunk c ^ sw(r), sw(r) = 2*(r%4) + (r/4)%2. With 64 banks this
-// keeps the 16-row score reads and the 4-row transposing reads conflict-free.
+// c is stored at chunk c ^ sw(r) (see tile_swz), which keeps the 16-row score
+// reads and the 4-row transposing reads free of bank conflicts on 64 banks.
 #pragma once
 
 #include "common.hpp"
@@ -72,7 +72,14 @@ struct MlaCfg {
     static_assert(48 * ROW_BYTES + 128 * ((CB - 1) / 4) < 65536, "value read offsets");
 };
 
-__device__ __forceinline__ int tile_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Chunk swizzle of tile row r. A tile row is an odd multiple of 128 bytes for
+// the compiled widths, so with 64 four-byte banks the row's parity picks the
+// bank half and the swizzle picks the 16-byte bank group within it:
+//   score reads (16 rows, one logical chunk): swz takes 8 distinct values on the
+//     even rows and on the odd rows of any 16 aligned rows;
+//   transposing reads (4 rows x 2 adjacent chunks per 16 lanes): swz >> 1 takes
+//     4 distinct values on the even and on the odd rows of any 8 aligned rows.
+__device__ __forceinline__ int tile_swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
 
 template <int K, int P>
 __global__ void __launch_bounds__(512, 1)
@@ -113,7 +120,7 @@ __global__ void __launch_bounds__(512, 1)
     const int sq = tile_swz(n);
     const int qk_off0 = (hc * 32 + n) * C::ROW_BYTES + ((g ^ sq) << 4);        // even k-steps
     const int qk_off1 = (hc * 32 + n) * C::ROW_BYTES + (((4 + g) ^ sq) << 4);  // odd k-steps
-    const int st = ((n >> 2) << 1) | (g & 1);
+    const int st = tile_swz(4 * g + (n >> 2));  // swizzle of the transposing reads' rows (same for +16, +32)
     const int hsel = (n & 3) >> 1;
     const int tr_row = (4 * g + (n >> 2)) * C::ROW_BYTES + ((n & 1) << 3);
     int tr_off[4];

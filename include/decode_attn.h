@@ -95,15 +95,16 @@ size_t mla_decode_workspace_size(int b, int s, int h, int k, int p, int t_max, i
  *                            mla_decode_workspace_size(b, s, h, k, p, t_max, num_workers)
  *                            bytes, 256-byte aligned; its contents on entry do not matter.
  * Compiled set: (k, p) in {(512, 64), (256, 64), (128, 64), (64, 16)}, h >= 1,
- * s * h <= 65536.
+ * s * h <= 65536, t_max * (k + p) * 2 < 2^31.
  */
 da_status mla_decode(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *cache,
                      const int32_t *seqlens, int b, int s, int h, int k, int p, int t_max,
                      float scale, uint16_t *out_lat, float *lse, void *workspace,
                      size_t workspace_bytes, int num_workers, void *stream);
 
-/* Bytes of workspace gqa_decode needs (0 for arguments gqa_decode would reject). */
-size_t gqa_decode_workspace_size(int b, int s, int hq, int hkv, int d, int t_max, int num_workers);
+/* Bytes of workspace gqa_decode needs for these shapes, num_workers and path
+ * (0 for arguments gqa_decode would reject). */
+size_t gqa_decode_workspace_size(int b, int s, int hq, int hkv, int d, int t_max, int num_workers, int path);
 
 /*
  * Grouped-query decode (MHA when hkv == hq, MQA when hkv == 1).
@@ -114,10 +115,11 @@ size_t gqa_decode_workspace_size(int b, int s, int hq, int hkv, int d, int t_max
  *   out     [b, s, hq, d]      bf16
  *   lse     [b, s, hq]         fp32 (natural log)
  * Query head hh reads K/V head hh / (hq / hkv).
- * Compiled set: d in {64, 128, 256}; (hq / hkv) * s <= 64.
- * `path`: 0 = automatic (VALU dot kernel when (hq/hkv)*s < 16, MFMA kernel
- * otherwise), 1 = force the VALU kernel (needs (hq/hkv)*s <= 16),
- * 2 = force the MFMA kernel.
+ * Compiled set: d in {64, 128, 256}; R = (hq / hkv) * s query rows per K/V
+ * head with R <= 64 (R <= 32 for d = 256); t_max * hkv * d * 2 < 2^31.
+ * `path` selects the kernel: 1 = VALU dot kernel (R <= 16), 2 = MFMA kernel
+ * (rows padded to blocks of 16), 0 = automatic (VALU when R < 16, MFMA
+ * otherwise). Both give the same result up to fp32 rounding.
  */
 da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
                      const int32_t *seqlens, int b, int s, int hq, int hkv, int d, int t_max,

@@ -31,7 +31,7 @@ def lib():
     P, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     L.da_status_string.argtypes, L.da_status_string.restype = [I], ctypes.c_char_p
     L.mla_decode_workspace_size.argtypes, L.mla_decode_workspace_size.restype = [I] * 7, Z
-    L.gqa_decode_workspace_size.argtypes, L.gqa_decode_workspace_size.restype = [I] * 7, Z
+    L.gqa_decode_workspace_size.argtypes, L.gqa_decode_workspace_size.restype = [I] * 8, Z
     L.mla_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, P]
     L.gqa_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, I, P]
     return L
@@ -96,7 +96,9 @@ def test_mla_rejects(lib, kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(hq=6, hkv=4), DA_ERR_INVALID_ARG),
     (dict(d=96), DA_ERR_UNSUPPORTED),
-    (dict(hq=64, hkv=1, s=2), DA_ERR_UNSUPPORTED),
+    (dict(hq=64, hkv=1, s=2), DA_ERR_UNSUPPORTED),      # 128 rows per KV head
+    (dict(hq=32, hkv=1, s=1, path=1), DA_ERR_UNSUPPORTED),  # VALU kernel takes at most 16 rows
+    (dict(t=1 << 20, hkv=8, d=256), DA_ERR_UNSUPPORTED),   # 32-bit buffer offsets
     (dict(path=7), DA_ERR_INVALID_ARG),
     (dict(v=None), DA_ERR_INVALID_ARG),
     (dict(s=0), DA_ERR_INVALID_ARG),
@@ -108,7 +110,8 @@ def test_gqa_rejects(lib, kw, code):
 def test_workspace_size_zero_for_rejected_args(lib):
     assert lib.mla_decode_workspace_size(0, 1, 16, 512, 64, 128, 0) == 0
     assert lib.mla_decode_workspace_size(2, 1, 16, 100, 64, 128, 0) == 0
-    assert lib.gqa_decode_workspace_size(2, 1, 6, 4, 128, 128, 0) == 0
+    assert lib.gqa_decode_workspace_size(2, 1, 6, 4, 128, 128, 0, 0) == 0
+    assert lib.gqa_decode_workspace_size(2, 1, 8, 2, 128, 128, 0, 5) == 0
 
 
 def test_workspace_size_explicit_workers(lib):

@@ -173,7 +173,8 @@ def run_gqa(da, shape, tensors, num_workers=0, path=0):
     q, k, v, sl = tensors
     d = dev()
     g = [t.to(d) for t in (q, k, v, sl)]
-    nbytes = da.gqa_decode_workspace_size(shape.b, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max, num_workers)
+    nbytes = da.gqa_decode_workspace_size(shape.b, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max, num_workers,
+                                          path)
     ws = poisoned(nbytes, d)
     out, lse = da.gqa_decode(*g, shape.scale, num_workers=num_workers, path=path, workspace=ws)
     torch.cuda.synchronize()
@@ -188,38 +189,60 @@ GQA_SMALL = [
     (2, 1, 32, 4, 256, 96, [96, 33]),       # d = 256, group 8
     (2, 2, 16, 2, 128, 300, [0, 299]),      # group 8 x 2 drafts = 16 rows, empty sequence
     (1, 1, 6, 3, 128, 70, [70]),            # group 2
+    (2, 4, 16, 2, 128, 200, [200, 131]),    # 32 rows per KV head
+    (2, 8, 64, 8, 64, 100, [100, 9]),       # 64 rows per KV head, d = 64
+    (3, 1, 64, 8, 128, 520, [520, 1, 257]),  # the layer's geometry, ragged
+    (1, 4, 32, 4, 256, 64, [64]),            # d = 256, 32 rows
 ]
 
 
-@pytest.mark.parametrize("case", GQA_SMALL, ids=lambda c: "b%d_s%d_hq%d_hkv%d_d%d" % c[:5])
+def gqa_paths(case):
+    rows = case[2] // case[3] * case[1]
+    return [1, 2] if rows <= 16 else [2]
+
+
+@pytest.mark.parametrize("case,path", [(c, p) for c in GQA_SMALL for p in gqa_paths(c)],
+                         ids=lambda x: ("b%d_s%d_hq%d_hkv%d_d%d" % x[:5]) if isinstance(x, tuple) else "path%d" % x)
 @pytest.mark.parametrize("workers", [0, 1, 5])
-def test_gqa_small(da, oracle_mod, case, workers):
+def test_gqa_small(da, oracle_mod, case, path, workers):
     b, s, hq, hkv, d, t, sl = case
     shape = wl.GQAShape(b=b, s=s, hq=hq, hkv=hkv, d=d, t_max=t, scale=1.0 / math.sqrt(d), seed=200 + hq + d)
     tensors = wl.make_gqa(shape, seqlens=sl)
-    print("gqa small", case, "workers", workers, flush=True)
-    out, lse = run_gqa(da, shape, tensors, workers)
+    print("gqa small", case, "path", path, "workers", workers, flush=True)
+    out, lse = run_gqa(da, shape, tensors, workers, path)
     ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale)
-    compare(out, lse, ref_o, ref_l, "gqa %s w=%d" % (case, workers))
+    compare(out, lse, ref_o, ref_l, "gqa %s path=%d w=%d" % (case, path, workers))
 
 
-def test_gqa_layer_full_size(da, oracle_mod):
+@pytest.mark.parametrize("path", [1, 2])
+def test_gqa_layer_full_size(da, oracle_mod, path):
     shape = wl.GQA_LAYER
     tensors = wl.make_gqa(shape)
-    print("full-size gqa", flush=True)
-    out, lse = run_gqa(da, shape, tensors, 0)
+    print("full-size gqa path", path, flush=True)
+    out, lse = run_gqa(da, shape, tensors, 0, path)
     rows = wl.sample_rows(shape.rows, 512, shape.seed).numpy()
     ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale, rows=rows)
-    compare(out.reshape(-1, shape.d)[rows], lse.reshape(-1)[rows], ref_o, ref_l, "gqa full")
+    compare(out.reshape(-1, shape.d)[rows], lse.reshape(-1)[rows], ref_o, ref_l, "gqa full path=%d" % path)
 
 
-def test_gqa_mha_equals_repeated_kv(da):
+@pytest.mark.parametrize("path", [1, 2])
+def test_gqa_mha_equals_repeated_kv(da, path):
     """GQA equals MHA run on K/V heads repeated per group (GPU against GPU)."""
     shape = wl.GQAShape(b=2, s=1, hq=16, hkv=2, d=128, t_max=256, scale=1.0 / math.sqrt(128), seed=5)
     q, k, v, sl = wl.make_gqa(shape, seqlens=[256, 100])
-    o1, l1 = run_gqa(da, shape, (q, k, v, sl))
+    o1, l1 = run_gqa(da, shape, (q, k, v, sl), 0, path)
     mha = wl.GQAShape(b=2, s=1, hq=16, hkv=16, d=128, t_max=256, scale=shape.scale, seed=5)
     o2, l2 = run_gqa(da, mha, (q, k.repeat_interleave(8, dim=2).contiguous(),
-                               v.repeat_interleave(8, dim=2).contiguous(), sl))
+                               v.repeat_interleave(8, dim=2).contiguous(), sl), 0, path)
+    assert (o1.float() - o2.float()).abs().max().item() <= 2 ** -7 * o1.float().abs().max().item()
+    assert (l1 - l2).abs().max().item() <= 1e-4
+
+
+def test_gqa_paths_agree(da):
+    """The VALU and MFMA kernels agree with each other on the layer's geometry."""
+    shape = wl.GQAShape(b=4, s=1, hq=64, hkv=8, d=128, t_max=1000, scale=1.0 / math.sqrt(128), seed=11)
+    tensors = wl.make_gqa(shape, seqlens=[1000, 999, 64, 513])
+    o1, l1 = run_gqa(da, shape, tensors, 0, 1)
+    o2, l2 = run_gqa(da, shape, tensors, 0, 2)
     assert (o1.float() - o2.float()).abs().max().item() <= 2 ** -7 * o1.float().abs().max().item()
     assert (l1 - l2).abs().max().item() <= 1e-4
