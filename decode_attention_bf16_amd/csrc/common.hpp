@@ -107,6 +107,17 @@ __device__ __forceinline__ float wave_sum_across_groups16(float v)
     return v;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's own LDS
+// operations, then s_barrier. Unlike __syncthreads() it does not drain
+// outstanding global loads (vmcnt), so HBM->LDS copies issued for later tiles
+// stay in flight across it; kernels wait for those copies explicitly (vmcnt)
+// before the barrier that publishes them. The "memory" clobber keeps the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ int clamp_len(int len, int t_max)
 {
     return len < 0 ? 0 : (len > t_max ? t_max : len);

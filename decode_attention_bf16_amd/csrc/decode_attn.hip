@@ -210,7 +210,8 @@ int gqa_choose_path(int rows, int path)
 {
     if (path == 1) return 0;
     if (path == 2) return 1;
-    return rows < 16 ? 0 : 1;
+    (void)rows;
+    return 1;  // measured faster at every row count (see the design notes)
 }
 
 }  // namespace

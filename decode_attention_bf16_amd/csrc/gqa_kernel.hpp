@@ -275,8 +275,8 @@ namespace da {
 //                                       score registers
 // LDS stage layout: 16 K token rows then 16 V token rows of 1 KB (the block's
 // heads, d contiguous); 16-byte chunk c of token row t is stored at
-// c ^ gsw(t), gsw(t) = (t & 15) ^ ((t & 1) << 3), which keeps the 16-token score
-// reads and the 4-token transposing reads free of bank conflicts on 64 banks.
+// c ^ gqa_swz(t), which keeps the score reads and the transposing reads free of
+// bank conflicts on 64 banks.
 template <int D, int RBLK>
 struct GqaMfmaCfg {
     static_assert(D == 64 || D == 128 || D == 256, "head dim");
@@ -292,7 +292,16 @@ struct GqaMfmaCfg {
     static constexpr int DB = D / 16;            // 16-wide output blocks
 };
 
-__device__ __forceinline__ int gqa_swz(int t) { return (t & 15) ^ ((t & 1) << 3); }
+// XOR applied to the chunk index (low four bits) of token row t of a stage. A
+// linear map of the token's low four bits (bit 2 ^= bit 0, bit 3 ^= bit 0 ^ bit 1),
+// chosen by checking this kernel's access patterns on the CPU: the 16-token
+// score reads and the 4-token transposing reads use 64 distinct banks under
+// every plausible grouping of the lanes into passes.
+__device__ __forceinline__ int gqa_swz(int t)
+{
+    t &= 15;
+    return t ^ ((t & 1) << 2) ^ ((((t >> 1) ^ t) & 1) << 3);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
@@ -456,7 +465,7 @@ __global__ void __launch_bounds__(64 * (512 / D), 1)
             wait_vmcnt<C::LW>();
         else
             wait_vmcnt<0>();
-        __syncthreads();
+        lds_barrier();
         if (sg + 3 < nst) issue_stage(sg + 3);
 
         const int tok0 = (tt - ts_cur) * kGqaTile + (sg % SUB) * C::T;

@@ -72,14 +72,20 @@ struct MlaCfg {
     static_assert(48 * ROW_BYTES + 128 * ((CB - 1) / 4) < 65536, "value read offsets");
 };
 
-// Chunk swizzle of tile row r. A tile row is an odd multiple of 128 bytes for
-// the compiled widths, so with 64 four-byte banks the row's parity picks the
-// bank half and the swizzle picks the 16-byte bank group within it:
-//   score reads (16 rows, one logical chunk): swz takes 8 distinct values on the
-//     even rows and on the odd rows of any 16 aligned rows;
-//   transposing reads (4 rows x 2 adjacent chunks per 16 lanes): swz >> 1 takes
-//     4 distinct values on the even and on the odd rows of any 8 aligned rows.
-__device__ __forceinline__ int tile_swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+// Chunk swizzle of tile row r: logical 16-byte chunk c of row r is stored at
+// c ^ tile_swz(r) (the low three bits, i.e. within its 128-byte group). A tile
+// row is an odd multiple of 128 bytes, so with 64 four-byte banks the row's
+// parity picks the bank half and the swizzle the 16-byte group inside it. The
+// map is linear in bits 1..3 of r (columns 3, 4, 5 for bits 1, 2, 3) and was
+// chosen, by checking every access pattern of this kernel on the CPU, so that
+// the 16-row score reads (ds_read_b128) and the 4-row transposing reads
+// (ds_read_b64_tr_b16) hit 64 distinct banks under every plausible grouping of
+// the 64 lanes into 16- or 32-lane passes (contiguous, or lanes l and l+32).
+__device__ __forceinline__ int tile_swz(int r)
+{
+    const int i0 = (r >> 1) & 1, i1 = (r >> 2) & 1, i2 = (r >> 3) & 1;
+    return (i0 ^ i2) | (i0 << 1) | ((i1 ^ i2) << 2);
+}
 
 template <int K, int P>
 __global__ void __launch_bounds__(512, 1)
@@ -242,7 +248,7 @@ __global__ void __launch_bounds__(512, 1)
     issue_tile(bcur, tile_lo - ts_cur, 0);
     begin_segment(bcur);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    lds_barrier();
 
     for (int tt = tile_lo; tt < tile_hi; ++tt) {
         const int cbuf = (tt - tile_lo) & 1;
@@ -302,7 +308,7 @@ __global__ void __launch_bounds__(512, 1)
             *(DA_LDS float *)(xme + 1088 + n * 4) = mloc;
         }
         if (lane == 0) *(DA_LDS int *)(lds + C::FLAG_OFF + w * 4) = need;
-        __syncthreads();
+        lds_barrier();
         // s_barrier is block-wide: the repair round (one more barrier) is taken
         // by every wave whenever any wave asks for it; only the pairs that asked
         // change anything.
@@ -325,7 +331,7 @@ __global__ void __launch_bounds__(512, 1)
                 *(DA_LDS u32x4 *)(xme + lane * 16) = pown;
                 if (g == 0) *(DA_LDS float *)(xme + 1024 + n * 4) = part;
             }
-            __syncthreads();
+            lds_barrier();
         }
         const u32x4 ppar = *(const DA_LDS u32x4 *)(xpa + lane * 16);
         lsum += part + *(const DA_LDS float *)(xpa + 1024 + n * 4);
@@ -362,7 +368,7 @@ __global__ void __launch_bounds__(512, 1)
 
         // ---- next tile landed in LDS; everybody is done with this one and the exchange slots
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        lds_barrier();
 
         const bool seg_ends = (tt + 1 == tile_hi) || (tt + 1 >= te_cur);
         if (seg_ends) {

@@ -118,8 +118,8 @@ size_t gqa_decode_workspace_size(int b, int s, int hq, int hkv, int d, int t_max
  * Compiled set: d in {64, 128, 256}; R = (hq / hkv) * s query rows per K/V
  * head with R <= 64 (R <= 32 for d = 256); t_max * hkv * d * 2 < 2^31.
  * `path` selects the kernel: 1 = VALU dot kernel (R <= 16), 2 = MFMA kernel
- * (rows padded to blocks of 16), 0 = automatic (VALU when R < 16, MFMA
- * otherwise). Both give the same result up to fp32 rounding.
+ * (rows padded to blocks of 16), 0 = automatic (currently the MFMA kernel for
+ * every R). Both give the same result up to fp32 rounding.
  */
 da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
                      const int32_t *seqlens, int b, int s, int hq, int hkv, int d, int t_max,
