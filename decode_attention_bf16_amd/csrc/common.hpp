@@ -118,6 +118,48 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Wait until at most N of this wave's vector memory operations are in flight
+// (loads return in issue order, so this retires all but the N newest).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// s_waitcnt vmcnt(0) issued through the builtin, so that the compiler's own
+// wait tracking sees it (encoding: vmcnt 0, expcnt 7 and lgkmcnt 15 = no wait).
+// Used right after a wave's register loads that precede a long loop of copies
+// issued with lds_dma16: the compiler does not know about those copies, and
+// without this it would re-wait for the loads, hence for every copy in flight,
+// at each use of the loaded registers inside the loop.
+__device__ __forceinline__ void wait_vm_loads_visible() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Buffer resource for raw (unswizzled, stride 0) byte addressing of
+// [base, base + num_bytes): accesses at offsets >= num_bytes read as zero.
+__device__ __forceinline__ u32x4 raw_buffer_rsrc(const void *base, uint32_t num_bytes)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, num_bytes, 0x00020000u};
+}
+
+// HBM -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane i
+// reads rsrc bytes [voffset, voffset + 16) and writes LDS bytes
+// [lds_base + 16 i, + 16). The copy has no register results; its LDS writes
+// are ordered by the caller with wait_vmcnt (loads retire in issue order)
+// followed by a barrier. Written as inline assembly because the compiler,
+// which cannot tell the copy's LDS destination apart from the buffers the
+// wave reads meanwhile, would otherwise wait for every copy in flight before
+// the wave's next LDS read and so undo the multi-buffering. M0 carries the LDS
+// base; one wait state separates writing M0 from the copy that reads it.
+__device__ __forceinline__ void lds_dma16(const u32x4 &rsrc, const DA_LDS void *lds_base, uint32_t voffset)
+{
+    const uint32_t m0 = (uint32_t)(uintptr_t)lds_base;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voffset), "s"(rsrc)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ int clamp_len(int len, int t_max)
 {
     return len < 0 ? 0 : (len > t_max ? t_max : len);

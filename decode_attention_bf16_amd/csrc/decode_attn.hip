@@ -52,9 +52,7 @@ bool log_plan()
 }
 
 // ------------------------------------------------------------------ MLA
-constexpr int kMlaRows = 64;
-
-int mla_row_blocks(int s, int h) { return (s * h + kMlaRows - 1) / kMlaRows; }
+int mla_row_blocks(int s, int h) { return (s * h + da::kMlaRows - 1) / da::kMlaRows; }
 
 int mla_workers(int b, int s, int h, int t_max, int requested)
 {
@@ -63,7 +61,7 @@ int mla_workers(int b, int s, int h, int t_max, int requested)
     int w = current_cu_count() / rb;
     if (w < 1) w = 1;
     // never more workers than tiles could exist
-    const long max_tiles = (long)b * ((t_max + 63) / 64);
+    const long max_tiles = (long)b * ((t_max + da::kMlaTile - 1) / da::kMlaTile);
     if ((long)w > max_tiles) w = (int)max_tiles;
     return w < 1 ? 1 : w;
 }

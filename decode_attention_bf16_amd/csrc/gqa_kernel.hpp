@@ -303,8 +303,6 @@ __device__ __forceinline__ int gqa_swz(int t)
     return t ^ ((t & 1) << 2) ^ ((((t >> 1) ^ t) & 1) << 3);
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 template <int D, int RBLK>
 __global__ void __launch_bounds__(64 * (512 / D), 1)
@@ -368,10 +366,10 @@ __global__ void __launch_bounds__(64 * (512 / D), 1)
             const int r = w + i * C::HPB;  // wave-uniform
             const int tk = r & 15;
             const uint16_t *base = (r < 16 ? kc : vc) + (size_t)bq * t_max * tok_elems;
-            __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, nrec, 0x00020000);
+            const u32x4 rsrc = raw_buffer_rsrc(base, (uint32_t)nrec);
             const int c = lane ^ gqa_swz(tk);
             const uint32_t off = (uint32_t)(((tok0 + tk) * (int)tok_elems + hb * C::HPB * D) * 2 + c * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (DA_LDS void *)(dst + r * C::ROWB), 16, (int)off, 0, 0, 0);
+            lds_dma16(rsrc, dst + r * C::ROWB, off);
         }
     };
 
@@ -408,6 +406,7 @@ __global__ void __launch_bounds__(64 * (512 / D), 1)
         }
         for (int off = 1; off < 64; off <<= 1) mn = min(mn, __shfl_xor(mn, off));
         nvis_min = mn;
+        wait_vm_loads_visible();
     };
     auto end_segment = [&](int bq, int first_tile_of_seq) {
         if (!active) return;
@@ -439,13 +438,13 @@ __global__ void __launch_bounds__(64 * (512 / D), 1)
         }
     };
 
-    // ---- prologue
-    for (int sg = 0; sg < min(3, nst); ++sg) issue_stage(sg);
+    // ---- prologue (queries first: their wait then drains nothing else)
     int bcur = find_sequence(tile_start, B, tile_lo);
     int ts_cur = tile_start[bcur];
     int te_cur = tile_start[bcur + 1];
     int L = clamp_len(seqlens[bcur], t_max);
     begin_segment(bcur);
+    for (int sg = 0; sg < min(3, nst); ++sg) issue_stage(sg);
 
     for (int sg = 0; sg < nst; ++sg) {
         const int tt = tile_lo + sg / SUB;
