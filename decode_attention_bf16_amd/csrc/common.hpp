@@ -92,19 +92,43 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+// Reductions over lanes l, l^16, l^32 and l^48 with the gfx950 lane-swap
+// instructions (VALU, no LDS round trip). v_permlane16_swap applied to (v, v)
+// returns two values whose pair, on every lane, is {v[l], v[l^16]} (in one
+// order or the other), and v_permlane32_swap likewise {v[l], v[l^32]}; a
+// commutative combine of the pair is therefore identical on both lanes.
+struct LanePair {
+    float a, b;
+};
+// The element copies into scalars matter: with this compiler a bit cast applied
+// directly to a subscripted vector element reads element 0.
+__device__ __forceinline__ LanePair swap16_pair(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                    false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    return {__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1)};
+}
+__device__ __forceinline__ LanePair swap32_pair(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                    false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    return {__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1)};
+}
+
 __device__ __forceinline__ float wave_max_across_groups16(float v)
 {
-    // max over lanes l, l^16, l^32, l^48
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    const LanePair x = swap16_pair(v);
+    const LanePair y = swap32_pair(fmaxf(x.a, x.b));
+    return fmaxf(y.a, y.b);
 }
 
 __device__ __forceinline__ float wave_sum_across_groups16(float v)
 {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    const LanePair x = swap16_pair(v);
+    const LanePair y = swap32_pair(x.a + x.b);
+    return y.a + y.b;
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's own LDS
@@ -134,6 +158,13 @@ __device__ __forceinline__ void wait_vmcnt()
 // at each use of the loaded registers inside the loop.
 __device__ __forceinline__ void wait_vm_loads_visible() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt lgkmcnt(0) through the builtin (vmcnt 63 and expcnt 7 = no wait).
+// Placed at the end of a rarely taken branch that issues scalar loads, so that
+// the join after the branch does not inherit their pending count: otherwise
+// the compiler waits there for everything lgkmcnt covers, including the LDS
+// reads the wave issued just before.
+__device__ __forceinline__ void wait_lgkm_visible() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Buffer resource for raw (unswizzled, stride 0) byte addressing of
 // [base, base + num_bytes): accesses at offsets >= num_bytes read as zero.
 __device__ __forceinline__ u32x4 raw_buffer_rsrc(const void *base, uint32_t num_bytes)
@@ -150,14 +181,15 @@ __device__ __forceinline__ u32x4 raw_buffer_rsrc(const void *base, uint32_t num_
 // which cannot tell the copy's LDS destination apart from the buffers the
 // wave reads meanwhile, would otherwise wait for every copy in flight before
 // the wave's next LDS read and so undo the multi-buffering. M0 carries the LDS
-// base; one wait state separates writing M0 from the copy that reads it.
+// base (an input operand, so the compiler writes it and knows it is live); one
+// wait state separates writing M0 from the copy that reads it.
 __device__ __forceinline__ void lds_dma16(const u32x4 &rsrc, const DA_LDS void *lds_base, uint32_t voffset)
 {
     const uint32_t m0 = (uint32_t)(uintptr_t)lds_base;
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
-                 : "s"(m0), "v"(voffset), "s"(rsrc)
-                 : "memory", "m0");
+                 : "v"(voffset), "s"(rsrc), "{m0}"(m0)
+                 : "memory");
 }
 
 __device__ __forceinline__ int clamp_len(int len, int t_max)

@@ -63,6 +63,7 @@ struct MlaCfg {
     static constexpr int LPW = T * ROW_CHUNKS / 256;            // copy instructions per value wave per tile
     static_assert(T * ROW_CHUNKS % 256 == 0, "tile chunks divisible among the four copying waves");
     static constexpr int CBV = K / 64;                          // 16-column output blocks per value wave
+    static constexpr int QCH = 3;                               // score k-steps per LDS read chunk
     static constexpr int PBUF_OFF = NBUF * TILE_BYTES;          // [2 slots][4 row blocks][64 lanes] x 16 B
     static constexpr int ALPHA_OFF = PBUF_OFF + 2 * 4 * 64 * 16;  // [2 slots][64 rows] float
     static constexpr int FLAG_OFF = ALPHA_OFF + 2 * 64 * 4;       // [2 slots][4 row blocks] int
@@ -99,6 +100,7 @@ struct SeqCursor {
             b = find_sequence(tile_start, B, tt);
             ts = tile_start[b];
             te = tile_start[b + 1];
+            wait_lgkm_visible();
         }
     }
 };
@@ -182,22 +184,41 @@ __global__ void __launch_bounds__(512, 1)
                 }
                 const DA_LDS char *tile = lds + (j % C::NBUF) * C::TILE_BYTES;
 
-                // S^T[32 tokens, 16 rows]
+                // S^T[32 tokens, 16 rows]. The tile's A fragments are read in
+                // chunks of QCH k-steps, two chunks ahead of the MFMAs that use
+                // them, so LDS latency hides behind matrix work.
                 f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
                 {
-                    bf16x8 a0 = *(const DA_LDS bf16x8 *)(tile + qk_off0);
-                    bf16x8 a1 = *(const DA_LDS bf16x8 *)(tile + qk_off0 + 16 * C::ROW_BYTES);
+                    constexpr int QCH = C::QCH;
+                    constexpr int NQC = (C::KSTEPS + QCH - 1) / QCH;
+                    bf16x8 af[2][2 * QCH];
+                    auto load_chunk = [&](int c, bf16x8(&d)[2 * QCH]) {
 #pragma unroll
-                    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-                        const bf16x8 b0 = a0, b1 = a1;
-                        if (kk + 1 < C::KSTEPS) {
-                            const DA_LDS char *nb =
-                                tile + (((kk + 1) & 1) ? qk_off1 : qk_off0) + 128 * ((kk + 1) >> 1);
-                            a0 = *(const DA_LDS bf16x8 *)(nb);
-                            a1 = *(const DA_LDS bf16x8 *)(nb + 16 * C::ROW_BYTES);
+                        for (int i = 0; i < QCH; ++i) {
+                            const int kk = c * QCH + i;
+                            if (kk < C::KSTEPS) {
+                                const DA_LDS char *p = tile + ((kk & 1) ? qk_off1 : qk_off0) + 128 * (kk >> 1);
+                                d[2 * i] = *(const DA_LDS bf16x8 *)(p);
+                                d[2 * i + 1] = *(const DA_LDS bf16x8 *)(p + 16 * C::ROW_BYTES);
+                            }
                         }
-                        S[0] = mfma16x16x32(b0, qB[kk], S[0]);
-                        S[1] = mfma16x16x32(b1, qB[kk], S[1]);
+                    };
+                    load_chunk(0, af[0]);
+                    if (NQC > 1) load_chunk(1, af[1]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int c = 0; c < NQC; ++c) {
+#pragma unroll
+                        for (int i = 0; i < QCH; ++i) {
+                            const int kk = c * QCH + i;
+                            if (kk < C::KSTEPS) {
+                                S[0] = mfma16x16x32(af[c & 1][2 * i], qB[kk], S[0]);
+                                S[1] = mfma16x16x32(af[c & 1][2 * i + 1], qB[kk], S[1]);
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (c + 2 < NQC) load_chunk(c + 2, af[c & 1]);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
                 // draft / length mask, only on tiles that reach past some row's visible end
@@ -271,10 +292,16 @@ __global__ void __launch_bounds__(512, 1)
 
         // HBM -> LDS copy of tile j of this worker into buffer j % NBUF
         SeqCursor dma;
+        int dma_b = -1, dma_len = 0;
         auto issue_tile = [&](int j) {
             const int tt = tile_lo + j;
             dma.seek(tile_start, B, tt);
-            const int L = clamp_len(seqlens[dma.b], t_max);
+            if (dma.b != dma_b) {
+                dma_b = dma.b;
+                dma_len = clamp_len(seqlens[dma.b], t_max);
+                wait_lgkm_visible();
+            }
+            const int L = dma_len;
             const u32x4 rsrc = raw_buffer_rsrc(cache + (size_t)dma.b * t_max * C::KP, (uint32_t)L * C::KP * 2);
             const uint32_t tile_bytes_in_seq = (uint32_t)(tt - dma.ts) * C::T * C::KP * 2;
 #pragma unroll
@@ -305,11 +332,31 @@ __global__ void __launch_bounds__(512, 1)
         lds_barrier();  // tile 0 has landed
         for (int j = 0; j <= ntiles; ++j) {
             const bool issued = j + 2 < ntiles;
-            if (issued) issue_tile(j + 2);
             bool stored = false;
+            const int tt = tile_lo + j - 1;
+            const int slot = (j - 1) & 1;
+            const DA_LDS char *tile = lds + ((j + C::NBUF - 1) % C::NBUF) * C::TILE_BYTES;
+            // all LDS reads of the step first (flags, probabilities, then every
+            // transposed latent fragment), the copy and the matrix work after them
+            u32x4 fl = {0u, 0u, 0u, 0u};
+            bf16x8 pB[4];
+            i16x4 vlo[C::CBV], vhi[C::CBV];
             if (j >= 1) {
-                const int tt = tile_lo + j - 1;
-                const int slot = (j - 1) & 1;
+                fl = *(const DA_LDS u32x4 *)(flag_buf + slot * 4);
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    pB[r4] = *(const DA_LDS bf16x8 *)(pbuf + ((slot * 4 + r4) * 64 + lane) * 16);
+#pragma unroll
+                for (int cb = 0; cb < C::CBV; ++cb) {
+                    const DA_LDS char *vb = tile + tr_addr(cb);
+                    vlo[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(vb));
+                    vhi[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(vb + 16 * C::ROW_BYTES));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (issued) issue_tile(j + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            if (j >= 1) {
                 const bool new_seg = cur.b < 0 || tt >= cur.te;
                 cur.seek(tile_start, B, tt);
                 if (new_seg) {
@@ -319,7 +366,6 @@ __global__ void __launch_bounds__(512, 1)
                         for (int cb = 0; cb < C::CBV; ++cb) acc[r4][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
                 // rows whose reference maximum moved: bring the sums to the new reference
-                const u32x4 fl = *(const DA_LDS u32x4 *)(flag_buf + slot * 4);
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
                     if (fl[r4]) {
@@ -328,20 +374,10 @@ __global__ void __launch_bounds__(512, 1)
                         for (int cb = 0; cb < C::CBV; ++cb) acc[r4][cb] *= al;
                     }
                 }
-                bf16x8 pB[4];
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4)
-                    pB[r4] = *(const DA_LDS bf16x8 *)(pbuf + ((slot * 4 + r4) * 64 + lane) * 16);
-                const DA_LDS char *tile = lds + ((j - 1) % C::NBUF) * C::TILE_BYTES;
-                typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
 #pragma unroll
                 for (int cb = 0; cb < C::CBV; ++cb) {
-                    const DA_LDS char *vb = tile + tr_addr(cb);
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(vb));
-                    const i16x4 hi =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(vb + 16 * C::ROW_BYTES));
                     const bf16x8 a =
-                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[cb], vhi[cb], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) acc[r4][cb] = mfma16x16x32(a, pB[r4], acc[r4][cb]);
                 }
