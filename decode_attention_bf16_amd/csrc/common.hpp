@@ -31,13 +31,13 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Two floats -> one dword of two bf16 (round to nearest even), lo in bits 0..15.
+typedef __attribute__((ext_vector_type(2))) float f32x2v;
+
+// Two floats -> one dword of two bf16 (round to nearest even), lo in bits 0..15
+// (a single v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    __bf16 a = (__bf16)lo;
-    __bf16 b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(unsigned short, a) |
-           ((uint32_t)__builtin_bit_cast(unsigned short, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ uint16_t to_bf16_bits(float f)

@@ -230,16 +230,21 @@ __global__ void __launch_bounds__(512, 1)
                         for (int i = 0; i < 4; ++i)
                             if (tok0 + bt * 16 + g * 4 + i >= nvis) S[bt][i] = -INFINITY;
                 }
-                // online softmax of the 16 rows
+                // online softmax of the 16 rows. Lane (n, g) holds 8 scores of
+                // row n; the row's reference maximum mref is kept identical on
+                // the row's four lanes (g = 0..3). A lane-local test decides
+                // whether any reference must move (rare: mostly the first tile
+                // of a segment); only then is the row maximum formed across the
+                // four lanes. Row sums stay per lane until the segment ends.
                 float m = -INFINITY;
 #pragma unroll
                 for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) m = fmaxf(m, S[bt][i]);
-                const float mt = wave_max_across_groups16(m) * scale_log2;  // row max, log2 units
                 const int slot = j & 1;
-                const bool upd = __builtin_amdgcn_ballot_w64(mt > mref + kRescaleSlack) != 0;
+                const bool upd = __builtin_amdgcn_ballot_w64(m * scale_log2 > mref + kRescaleSlack) != 0;
                 if (upd) {
+                    const float mt = wave_max_across_groups16(m) * scale_log2;  // row max, log2 units
                     const float mnew = fmaxf(mref, mt);
                     const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref - mnew);
                     mref = mnew;
@@ -248,7 +253,6 @@ __global__ void __launch_bounds__(512, 1)
                 }
                 if (lane == 0) flag_buf[slot * 4 + sw] = upd ? 1 : 0;
                 const float ms = mref == -INFINITY ? 0.f : mref;
-                float part = 0.f;
                 uint32_t pk[4];
 #pragma unroll
                 for (int bt = 0; bt < 2; ++bt) {
@@ -256,16 +260,18 @@ __global__ void __launch_bounds__(512, 1)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         p[i] = fast_exp2(__builtin_fmaf(S[bt][i], scale_log2, -ms));
-                        part += p[i];
+                        lsum += p[i];
                     }
                     pk[2 * bt] = pack_bf16x2(p[0], p[1]);
                     pk[2 * bt + 1] = pack_bf16x2(p[2], p[3]);
                 }
-                lsum += wave_sum_across_groups16(part);
                 *(DA_LDS u32x4 *)(pbuf + ((slot * 4 + sw) * 64 + lane) * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-                if ((tt + 1 >= cur.te || j + 1 == ntiles) && g == 0) {
-                    seg_buf[(slot * 64 + sw * 16 + n) * 2 + 0] = mref;
-                    seg_buf[(slot * 64 + sw * 16 + n) * 2 + 1] = lsum;
+                if (tt + 1 >= cur.te || j + 1 == ntiles) {
+                    const float ls = wave_sum_across_groups16(lsum);
+                    if (g == 0) {
+                        seg_buf[(slot * 64 + sw * 16 + n) * 2 + 0] = mref;
+                        seg_buf[(slot * 64 + sw * 16 + n) * 2 + 1] = ls;
+                    }
                 }
             }
             lds_barrier();
@@ -290,10 +296,12 @@ __global__ void __launch_bounds__(512, 1)
             }
         };
 
-        // HBM -> LDS copy of tile j of this worker into buffer j % NBUF
+        // HBM -> LDS copy of tile j of this worker into buffer j % NBUF:
+        // copy_setup resolves the sequence, copy_part issues copy instruction
+        // `it` of this wave (LPW per wave per tile).
         SeqCursor dma;
         int dma_b = -1, dma_len = 0;
-        auto issue_tile = [&](int j) {
+        auto copy_setup = [&](int j, u32x4 &rsrc, uint32_t &tile_bytes_in_seq) {
             const int tt = tile_lo + j;
             dma.seek(tile_start, B, tt);
             if (dma.b != dma_b) {
@@ -301,18 +309,23 @@ __global__ void __launch_bounds__(512, 1)
                 dma_len = clamp_len(seqlens[dma.b], t_max);
                 wait_lgkm_visible();
             }
-            const int L = dma_len;
-            const u32x4 rsrc = raw_buffer_rsrc(cache + (size_t)dma.b * t_max * C::KP, (uint32_t)L * C::KP * 2);
-            const uint32_t tile_bytes_in_seq = (uint32_t)(tt - dma.ts) * C::T * C::KP * 2;
+            rsrc = raw_buffer_rsrc(cache + (size_t)dma.b * t_max * C::KP, (uint32_t)dma_len * C::KP * 2);
+            tile_bytes_in_seq = (uint32_t)(tt - dma.ts) * C::T * C::KP * 2;
+        };
+        auto copy_part = [&](int j, const u32x4 &rsrc, uint32_t tile_bytes_in_seq, int it) {
+            const int pch = (it * 4 + vw) * 64 + lane;  // physical chunk within the tile
+            const int r = pch / C::ROW_CHUNKS;
+            const int c = (pch - r * C::ROW_CHUNKS) ^ tile_swz(r);
+            const uint32_t off =
+                c < C::SRC_CHUNKS ? (uint32_t)((r * C::KP + c * 8) * 2) + tile_bytes_in_seq : 0x80000000u;
+            lds_dma16(rsrc, lds + (j % C::NBUF) * C::TILE_BYTES + (it * 4 + vw) * 1024, off);
+        };
+        auto issue_tile = [&](int j) {
+            u32x4 rsrc;
+            uint32_t tbs;
+            copy_setup(j, rsrc, tbs);
 #pragma unroll
-            for (int it = 0; it < C::LPW; ++it) {
-                const int pch = (it * 4 + vw) * 64 + lane;  // physical chunk within the tile
-                const int r = pch / C::ROW_CHUNKS;
-                const int c = (pch - r * C::ROW_CHUNKS) ^ tile_swz(r);
-                const uint32_t off =
-                    c < C::SRC_CHUNKS ? (uint32_t)((r * C::KP + c * 8) * 2) + tile_bytes_in_seq : 0x80000000u;
-                lds_dma16(rsrc, lds + (j % C::NBUF) * C::TILE_BYTES + (it * 4 + vw) * 1024, off);
-            }
+            for (int it = 0; it < C::LPW; ++it) copy_part(j, rsrc, tbs, it);
         };
 
         f32x4 acc[4][C::CBV];
@@ -354,7 +367,15 @@ __global__ void __launch_bounds__(512, 1)
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (issued) issue_tile(j + 2);
+            // the copy of tile j+2 is spread over the matrix work below, so that
+            // a stall on a full memory queue overlaps MFMA execution
+            u32x4 crsrc = {0u, 0u, 0u, 0u};
+            uint32_t ctbs = 0;
+            if (issued) copy_setup(j + 2, crsrc, ctbs);
+            if (j == 0 && issued) {
+#pragma unroll
+                for (int it = 0; it < C::LPW; ++it) copy_part(j + 2, crsrc, ctbs, it);
+            }
             __builtin_amdgcn_sched_barrier(0);
             if (j >= 1) {
                 const bool new_seg = cur.b < 0 || tt >= cur.te;
@@ -380,6 +401,12 @@ __global__ void __launch_bounds__(512, 1)
                         __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[cb], vhi[cb], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) acc[r4][cb] = mfma16x16x32(a, pB[r4], acc[r4][cb]);
+                    if (issued) {
+#pragma unroll
+                        for (int it = 0; it < C::LPW; ++it)
+                            if ((it * C::CBV) / C::LPW == cb) copy_part(j + 2, crsrc, ctbs, it);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 // end of a segment: normalize and write the result or the partial
                 if (tt + 1 >= cur.te || j == ntiles) {
