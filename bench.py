@@ -153,9 +153,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-sample", type=float, default=0.5)
+    ap.add_argument("--cpu-sample", type=float, default=1.0,
+                    help="fraction of each workload's query rows the fp64 oracle baseline computes")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="s-sweep of MLA (one JSON line per s)")
+    ap.add_argument("--ragged", action="store_true", help="only the ragged long-context MLA workload")
     ap.add_argument("--only", default="", help="comma list of parts to run (gqa,mla_s1,mla_s4)")
     ap.add_argument("--gqa-path", type=int, default=0, help="GQA kernel: 0 auto, 1 VALU dot, 2 MFMA")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -180,6 +182,20 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n}), flush=True)
         return
     binding.load_library()
+
+    if args.ragged:
+        p = Part("mla_ragged", "mla", wl.MLA_RAGGED, dev)
+        wall, per = time_parts([p], args.steps, args.warmup)
+        sec = per[p.name]
+        c = cm.mla_absorbed_ragged(p.cpu[3].tolist(), p.shape.h, p.shape.s, p.shape.k, p.shape.p, p.shape.t_max,
+                                   masked=False)
+        t_min = cm.roofline_time(c)
+        print(json.dumps({"workload": "mla_ragged (b=64, s=1, h=128, k=512, p=64, seqlens U{1024..32768}, seed 4)",
+                          "us": round(sec * 1e6, 2), "tflops": round(c.flops / sec / 1e12, 2),
+                          "tbs": round(c.bytes / sec / 1e12, 3), "ai": round(c.ai, 1),
+                          "bound": "mfma" if c.ai > RIDGE else "hbm", "t_min_us": round(t_min * 1e6, 2),
+                          "roofline_frac": round(t_min / sec, 4)}), flush=True)
+        return
 
     if args.sweep:
         for s in wl.MTP_SWEEP:
@@ -237,6 +253,7 @@ def main():
         "step_roofline_frac": round(sum(p.t_min for p in parts) / wall, 4),
         "roofline": roof,
         "parts": part_info,
+        "kernel_source": kernel_source_hash(),
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(parts, args.cpu_sample)
