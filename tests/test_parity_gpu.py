@@ -144,6 +144,28 @@ def test_mla_garbage_beyond_seqlen_is_ignored(da, oracle_mod):
     compare(out, lse, ref_o, ref_l, "garbage rows")
 
 
+@pytest.mark.parametrize("workers", [1, 3])
+@pytest.mark.parametrize("late_row", [40, 150, 299])
+@pytest.mark.parametrize("mag", [6.0, 24.0])
+def test_mla_huge_late_score(da, oracle_mod, workers, late_row, mag):
+    """A cache row past a segment's first tile whose score exceeds every
+    earlier one by ~40 (mag 6) or ~160 (mag 24) powers of two: the kernel's
+    shared softmax reference must catch up (lazily, or by redoing the tile)
+    before that tile's probabilities are accumulated."""
+    shape = mla_shape(2, 2, 24, 512, 64, 300, seed=11)
+    ql, qr, c, sl = wl.make_mla(shape, seqlens=[300, 300])
+    big = torch.zeros(512 + 64)
+    big[:64] = mag
+    c[0, late_row] = big.to(torch.bfloat16)
+    c[1, late_row // 2] = (-big).to(torch.bfloat16)
+    c[1, (late_row + 77) % 300] = big.to(torch.bfloat16)
+    ql[0, :, :, :64] = torch.ones(64).to(torch.bfloat16)
+    ql[1, :, :, :64] = torch.ones(64).to(torch.bfloat16)
+    ref_o, ref_l = oracle_mod.mla(ql, qr, c, sl, shape.scale)
+    out, lse = run_mla(da, shape, (ql, qr, c, sl), workers)
+    compare(out, lse, ref_o, ref_l, "huge late score row %d workers %d" % (late_row, workers))
+
+
 # ------------------------------------------------------------------ MLA, full-size workloads, sampled rows
 def full_size_mla(da, oracle_mod, shape, n_rows=192):
     tensors = wl.make_mla(shape)
