@@ -49,51 +49,44 @@ static inline WsLayout ws_layout(int b, int rows_per_seq, int dv, int workers)
     return w;
 }
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 64;  // one wave: no block barriers on the planner's short critical path
 
-// Exclusive scan helper over the block: returns the exclusive prefix of `v`
-// across threads and the block total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int *sh, int &total)
+// Exclusive prefix sum of `v` across the wave's 64 lanes; `total` gets the sum.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int &total)
 {
-    const int tid = threadIdx.x;
-    sh[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        int add = tid >= off ? sh[tid - off] : 0;
-        __syncthreads();
-        sh[tid] += add;
-        __syncthreads();
+    const int lane = threadIdx.x & 63;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
     }
-    total = sh[kPlanThreads - 1];
-    int incl = sh[tid];
-    __syncthreads();
+    total = __shfl(incl, 63);
     return incl - v;
 }
 
-// One block of kPlanThreads threads. Each thread owns a contiguous run of
-// ceil(b / kPlanThreads) sequences.
+// One wave. Lane l owns a contiguous run of ceil(b / 64) sequences.
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t *__restrict__ seqlens, int b, int t_max,
                                                             int tile, int workers, PlanHeader *__restrict__ hdr,
                                                             int *__restrict__ tile_start,
                                                             int *__restrict__ slot_start)
 {
-    __shared__ int sh[kPlanThreads];
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x;
     const int chunk = (b + kPlanThreads - 1) / kPlanThreads;
-    const int lo = min(b, tid * chunk);
+    const int lo = min(b, lane * chunk);
     const int hi = min(b, lo + chunk);
 
     // Pass 1: tiles per sequence -> tile_start (exclusive prefix), total.
     int local = 0;
     for (int i = lo; i < hi; ++i) {
-        int L = clamp_len(seqlens[i], t_max);
+        const int L = clamp_len(seqlens[i], t_max);
         local += (L + tile - 1) / tile;
     }
     int total = 0;
-    int run = block_exclusive_scan(local, sh, total);
+    int run = wave_exclusive_scan(local, total);
     for (int i = lo; i < hi; ++i) {
         tile_start[i] = run;
-        int L = clamp_len(seqlens[i], t_max);
+        const int L = clamp_len(seqlens[i], t_max);
         run += (L + tile - 1) / tile;
     }
     const int per = max(1, (total + workers - 1) / workers);
@@ -101,25 +94,25 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t *__res
     // Pass 2: segments per sequence -> slot_start.
     int segs = 0;
     for (int i = lo; i < hi; ++i) {
-        int L = clamp_len(seqlens[i], t_max);
-        int nt = (L + tile - 1) / tile;
+        const int L = clamp_len(seqlens[i], t_max);
+        const int nt = (L + tile - 1) / tile;
         if (nt > 0) {
-            int first = tile_start[i];
+            const int first = tile_start[i];
             segs += (first + nt - 1) / per - first / per + 1;
         }
     }
     int segs_total = 0;
-    int srun = block_exclusive_scan(segs, sh, segs_total);
+    int srun = wave_exclusive_scan(segs, segs_total);
     for (int i = lo; i < hi; ++i) {
         slot_start[i] = srun;
-        int L = clamp_len(seqlens[i], t_max);
-        int nt = (L + tile - 1) / tile;
+        const int L = clamp_len(seqlens[i], t_max);
+        const int nt = (L + tile - 1) / tile;
         if (nt > 0) {
-            int first = tile_start[i];
+            const int first = tile_start[i];
             srun += (first + nt - 1) / per - first / per + 1;
         }
     }
-    if (tid == 0) {
+    if (lane == 0) {
         tile_start[b] = total;
         slot_start[b] = segs_total;
         hdr->total_tiles = total;
