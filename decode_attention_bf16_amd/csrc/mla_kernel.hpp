@@ -63,6 +63,10 @@ struct MlaCfg {
     static constexpr int LPW = T * ROW_CHUNKS / 256;            // copy instructions per value wave per tile
     static_assert(T * ROW_CHUNKS % 256 == 0, "tile chunks divisible among the four copying waves");
     static constexpr int CBV = K / 64;                          // 16-column output blocks per value wave
+    // value product with v_mfma_f32_32x32x16_bf16 (two chained 16-token k-steps
+    // per accumulator and tile) when a value wave's columns fill 32-column blocks
+    static constexpr bool WIDE = K % 128 == 0;
+    static constexpr int CB32 = K / 128;                        // 32-column output blocks per value wave
     static constexpr int QCH = 3;                               // score k-steps per LDS read chunk
     static constexpr int PBUF_OFF = NBUF * TILE_BYTES;          // [2 slots][4 row blocks][64 lanes] x 16 B
     static constexpr int ALPHA_OFF = PBUF_OFF + 2 * 4 * 64 * 16;  // [2 slots][64 rows] float
@@ -268,7 +272,17 @@ __global__ void __launch_bounds__(512, 1)
                     pk[2 * bt] = pack_bf16x2(p[0], p[1]);
                     pk[2 * bt + 1] = pack_bf16x2(p[2], p[3]);
                 }
-                *(DA_LDS u32x4 *)(pbuf + ((slot * 4 + sw) * 64 + lane) * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+                if constexpr (C::WIDE) {
+                    // B operand of the 32x32x16 value MFMA: [row block of 32][k-step][lane]
+                    // 16 bytes, lane l = row l%32 and tokens 16*ks + 8*(l/32) + 0..7
+                    const int l2 = 32 * (g >> 1) + 16 * (sw & 1) + n;
+#pragma unroll
+                    for (int bt = 0; bt < 2; ++bt)
+                        *(DA_LDS u32x2 *)(pbuf + ((((slot * 2 + (sw >> 1)) * 2 + bt) * 64 + l2) * 16 + 8 * (g & 1))) =
+                            u32x2{pk[2 * bt], pk[2 * bt + 1]};
+                } else {
+                    *(DA_LDS u32x4 *)(pbuf + ((slot * 4 + sw) * 64 + lane) * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+                }
                 if (tt + 1 >= cur.te || j + 1 == ntiles) {
                     const float ls = wave_sum_across_groups16(lsum);
                     if (g == 0) {
@@ -331,11 +345,37 @@ __global__ void __launch_bounds__(512, 1)
             for (int it = 0; it < C::LPW; ++it) copy_part(j, rsrc, tbs, it);
         };
 
-        f32x4 acc[4][C::CBV];
+        // accumulators: narrow form [16-row block][16-column block] (16x16x32),
+        // wide form [32-row block][32-column block] (32x32x16)
+        typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+        constexpr int NA4 = C::WIDE ? 1 : 4, NAC = C::WIDE ? 1 : C::CBV;
+        constexpr int NW2 = C::WIDE ? 2 : 1, NWC = C::WIDE ? C::CB32 : 1;
+        f32x4 acc[NA4][NAC];
+        f32x16 acw[NW2][NWC];
+        auto zero_acc = [&]() {
+            if constexpr (C::WIDE) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
+                for (int r = 0; r < NW2; ++r)
 #pragma unroll
-            for (int cb = 0; cb < C::CBV; ++cb) acc[r4][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int cb = 0; cb < NWC; ++cb)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) acw[r][cb][e] = 0.f;
+            } else {
+#pragma unroll
+                for (int r4 = 0; r4 < NA4; ++r4)
+#pragma unroll
+                    for (int cb = 0; cb < NAC; ++cb) acc[r4][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        };
+        zero_acc();
+        // wide form: byte offset (within a tile) of transposing read h of k-step
+        // ks for 32-column block cb; lane l gets tokens 16ks + 8(l/32) + 4h + 0..3
+        // of column 32cb + l%32 of this wave's columns
+        auto tr32_addr = [&](int cb, int ks, int h) -> int {
+            const int tok = 16 * ks + 8 * (g >> 1) + 4 * h + (n >> 2);
+            const int chunk = (vw * (K / 4) + 32 * cb) / 8 + 2 * (g & 1) + ((n >> 1) & 1);
+            return tok * C::ROW_BYTES + (((chunk & ~7) | ((chunk ^ tile_swz(tok)) & 7)) << 4) + ((n & 1) << 3);
+        };
         SeqCursor cur;
 
         issue_tile(0);
@@ -356,17 +396,28 @@ __global__ void __launch_bounds__(512, 1)
             // transposed latent fragment), the copy and the matrix work after them
             u32x4 fl = {0u, 0u, 0u, 0u};
             bf16x8 pB[4];
-            i16x4 vlo[C::CBV], vhi[C::CBV];
+            constexpr int NTR = C::WIDE ? 4 * C::CB32 : C::CBV;
+            i16x4 vlo[NTR], vhi[NTR];
             if (j >= 1) {
                 fl = *(const DA_LDS u32x4 *)(flag_buf + slot * 4);
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4)
                     pB[r4] = *(const DA_LDS bf16x8 *)(pbuf + ((slot * 4 + r4) * 64 + lane) * 16);
+                if constexpr (C::WIDE) {
 #pragma unroll
-                for (int cb = 0; cb < C::CBV; ++cb) {
-                    const DA_LDS char *vb = tile + tr_addr(cb);
-                    vlo[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(vb));
-                    vhi[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(vb + 16 * C::ROW_BYTES));
+                    for (int cb = 0; cb < C::CB32; ++cb)
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+                            vlo[2 * cb + ks] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(tile + tr32_addr(cb, ks, 0)));
+                            vhi[2 * cb + ks] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(tile + tr32_addr(cb, ks, 1)));
+                        }
+                } else {
+#pragma unroll
+                    for (int cb = 0; cb < C::CBV; ++cb) {
+                        const DA_LDS char *vb = tile + tr_addr(cb);
+                        vlo[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(vb));
+                        vhi[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(vb + 16 * C::ROW_BYTES));
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -383,63 +434,127 @@ __global__ void __launch_bounds__(512, 1)
             if (j >= 1) {
                 const bool new_seg = cur.b < 0 || tt >= cur.te;
                 cur.seek(tile_start, B, tt);
-                if (new_seg) {
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-                        for (int cb = 0; cb < C::CBV; ++cb) acc[r4][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
+                if (new_seg) zero_acc();
                 // rows whose reference maximum moved: bring the sums to the new reference
+                if (__builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3])) {
+                    if constexpr (C::WIDE) {
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    if (fl[r4]) {
-                        const float al = alpha_buf[slot * 64 + r4 * 16 + n];
+                        for (int r2 = 0; r2 < 2; ++r2) {
+                            const int r4 = 2 * r2 + (g & 1);  // this lane's 16-row block
+                            const float al = fl[r4] ? alpha_buf[slot * 64 + 16 * r4 + n] : 1.f;
 #pragma unroll
-                        for (int cb = 0; cb < C::CBV; ++cb) acc[r4][cb] *= al;
+                            for (int cb = 0; cb < C::CB32; ++cb) acw[r2][cb] *= al;
+                        }
+                    } else {
+#pragma unroll
+                        for (int r4 = 0; r4 < NA4; ++r4) {
+                            if (__builtin_amdgcn_readfirstlane(fl[r4])) {
+                                const float al = alpha_buf[slot * 64 + r4 * 16 + n];
+#pragma unroll
+                                for (int cb = 0; cb < NAC; ++cb) acc[r4][cb] *= al;
+                            }
+                        }
                     }
                 }
+                if constexpr (C::WIDE) {
+                    // pB[2 * r2 + ks] = B operand of 32-row block r2, k-step ks
 #pragma unroll
-                for (int cb = 0; cb < C::CBV; ++cb) {
-                    const bf16x8 a =
-                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[cb], vhi[cb], 0, 1, 2, 3, 4, 5, 6, 7));
+                    for (int cb = 0; cb < C::CB32; ++cb) {
+                        const bf16x8 a0 = __builtin_bit_cast(
+                            bf16x8, __builtin_shufflevector(vlo[2 * cb], vhi[2 * cb], 0, 1, 2, 3, 4, 5, 6, 7));
+                        const bf16x8 a1 = __builtin_bit_cast(
+                            bf16x8, __builtin_shufflevector(vlo[2 * cb + 1], vhi[2 * cb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) acc[r4][cb] = mfma16x16x32(a, pB[r4], acc[r4][cb]);
-                    if (issued) {
+                        for (int r2 = 0; r2 < 2; ++r2) {
+                            acw[r2][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, pB[2 * r2], acw[r2][cb], 0, 0, 0);
+                            acw[r2][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pB[2 * r2 + 1], acw[r2][cb], 0, 0, 0);
+                        }
+                        if (issued) {
 #pragma unroll
-                        for (int it = 0; it < C::LPW; ++it)
-                            if ((it * C::CBV) / C::LPW == cb) copy_part(j + 2, crsrc, ctbs, it);
+                            for (int it = 0; it < C::LPW; ++it)
+                                if ((it * C::CB32) / C::LPW == cb) copy_part(j + 2, crsrc, ctbs, it);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
+                } else {
+#pragma unroll
+                    for (int cb = 0; cb < C::CBV; ++cb) {
+                        const bf16x8 a = __builtin_bit_cast(
+                            bf16x8, __builtin_shufflevector(vlo[cb], vhi[cb], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) acc[r4][cb] = mfma16x16x32(a, pB[r4], acc[r4][cb]);
+                        if (issued) {
+#pragma unroll
+                            for (int it = 0; it < C::LPW; ++it)
+                                if ((it * C::CBV) / C::LPW == cb) copy_part(j + 2, crsrc, ctbs, it);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
                 // end of a segment: normalize and write the result or the partial
                 if (tt + 1 >= cur.te || j == ntiles) {
                     const int bq = cur.b;
                     const int nseg = slot_start[bq + 1] - slot_start[bq];
                     const int sl = slot_start[bq] + (worker - cur.ts / per);
-                    const int col0 = vw * (K / 4) + g * 4;
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int row = rb * C::ROWS + r4 * 16 + n;
-                        if (row >= M) continue;
-                        const float mr = seg_buf[(slot * 64 + r4 * 16 + n) * 2 + 0];
-                        const float ls = seg_buf[(slot * 64 + r4 * 16 + n) * 2 + 1];
-                        const float inv = ls > 0.f ? 1.f / ls : 0.f;
-                        const float lse2 = ls > 0.f ? mr + fast_log2(ls) : -INFINITY;
+                    // normalization of query row rloc (row of the block) and its output place
+                    auto row_info = [&](int rloc, float &inv, float &lse2) {
+                        const float mr = seg_buf[(slot * 64 + rloc) * 2 + 0];
+                        const float ls = seg_buf[(slot * 64 + rloc) * 2 + 1];
+                        inv = ls > 0.f ? 1.f / ls : 0.f;
+                        lse2 = ls > 0.f ? mr + fast_log2(ls) : -INFINITY;
+                    };
+                    auto put4 = [&](int row, int col, const f32x4 &v, float inv) {
                         if (nseg == 1) {
-                            uint16_t *o = out + ((size_t)bq * M + row) * K + col0;
-#pragma unroll
-                            for (int cb = 0; cb < C::CBV; ++cb) {
-                                u32x2 v;
-                                v[0] = pack_bf16x2(acc[r4][cb][0] * inv, acc[r4][cb][1] * inv);
-                                v[1] = pack_bf16x2(acc[r4][cb][2] * inv, acc[r4][cb][3] * inv);
-                                *(u32x2 *)(o + cb * 16) = v;
-                            }
-                            if (g == 0 && vw == 0) lse[(size_t)bq * M + row] = lse2 * kLn2;
+                            *(u32x2 *)(out + ((size_t)bq * M + row) * K + col) =
+                                u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
                         } else {
-                            float *o = part_out + ((size_t)sl * M + row) * K + col0;
+                            *(f32x4 *)(part_out + ((size_t)sl * M + row) * K + col) = v * inv;
+                        }
+                    };
+                    auto put_lse = [&](int row, float lse2) {
+                        // one writer per row: the wide layout spreads a row block over
+                        // lane groups 0 and 1, the narrow one keeps it in group 0
+                        if ((C::WIDE ? (g >> 1) : g) != 0 || vw != 0) return;
+                        if (nseg == 1)
+                            lse[(size_t)bq * M + row] = lse2 * kLn2;
+                        else
+                            part_lse[(size_t)sl * M + row] = lse2;
+                    };
+                    if constexpr (C::WIDE) {
 #pragma unroll
-                            for (int cb = 0; cb < C::CBV; ++cb) *(f32x4 *)(o + cb * 16) = acc[r4][cb] * inv;
-                            if (g == 0 && vw == 0) part_lse[(size_t)sl * M + row] = lse2;
+                        for (int r2 = 0; r2 < 2; ++r2) {
+                            // lane l: query row 32*r2 + l%32; value e of block cb is column
+                            // 32cb + 8(e/4) + 4(l/32) + e%4 of this wave's columns
+                            const int rloc = 32 * r2 + 16 * (g & 1) + n;
+                            const int row = rb * C::ROWS + rloc;
+                            if (row < M) {
+                                float inv, lse2;
+                                row_info(rloc, inv, lse2);
+                                const int col0 = vw * (K / 4) + 4 * (g >> 1);
+#pragma unroll
+                                for (int cb = 0; cb < C::CB32; ++cb)
+#pragma unroll
+                                    for (int qq = 0; qq < 4; ++qq)
+                                        put4(row, col0 + 32 * cb + 8 * qq,
+                                             f32x4{acw[r2][cb][4 * qq], acw[r2][cb][4 * qq + 1], acw[r2][cb][4 * qq + 2],
+                                                   acw[r2][cb][4 * qq + 3]},
+                                             inv);
+                                put_lse(row, lse2);
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const int rloc = 16 * r4 + n;
+                            const int row = rb * C::ROWS + rloc;
+                            if (row < M) {
+                                float inv, lse2;
+                                row_info(rloc, inv, lse2);
+                                const int col0 = vw * (K / 4) + g * 4;
+#pragma unroll
+                                for (int cb = 0; cb < C::CBV; ++cb) put4(row, col0 + 16 * cb, acc[r4][cb], inv);
+                                put_lse(row, lse2);
+                            }
                         }
                     }
                     stored = true;
