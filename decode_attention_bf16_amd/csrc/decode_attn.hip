@@ -112,6 +112,39 @@ hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint1
 int gqa_head_blocks(int hkv) { return (hkv + 3) / 4; }
 int gqa_choose_path(int rows, int path);
 
+// Launch shape of the MFMA kernel per head dim: KV heads per block and ring depth.
+#ifndef DA_GQA128_HPB
+#define DA_GQA128_HPB 4
+#endif
+#ifndef DA_GQA128_NST
+#define DA_GQA128_NST 4
+#endif
+template <int D>
+struct GqaMfmaShape {
+    static constexpr int HPB = D == 128 ? DA_GQA128_HPB : 512 / D;
+    static constexpr int NST = D == 128 ? DA_GQA128_NST : 4;
+};
+template <int D, int RBLK>
+using GqaMfmaCfgFor = da::GqaMfmaCfg<D, RBLK, GqaMfmaShape<D>::HPB, GqaMfmaShape<D>::NST>;
+
+// (heads per block, resident blocks per CU) of the MFMA kernel for head dim d
+void gqa_mfma_geometry(int d, int &hpb, int &per_cu)
+{
+    int lds = 0;
+    if (d == 64) {
+        hpb = GqaMfmaCfgFor<64, 1>::HPB;
+        lds = GqaMfmaCfgFor<64, 1>::LDS_BYTES;
+    } else if (d == 128) {
+        hpb = GqaMfmaCfgFor<128, 1>::HPB;
+        lds = GqaMfmaCfgFor<128, 1>::LDS_BYTES;
+    } else {
+        hpb = GqaMfmaCfgFor<256, 1>::HPB;
+        lds = GqaMfmaCfgFor<256, 1>::LDS_BYTES;
+    }
+    per_cu = 163840 / lds;
+    if (per_cu < 1) per_cu = 1;
+}
+
 int gqa_workers(int b, int hkv, int d, int rows, int path, int t_max, int requested)
 {
     if (requested > 0) return requested;
@@ -119,8 +152,9 @@ int gqa_workers(int b, int hkv, int d, int rows, int path, int t_max, int reques
     if (gqa_choose_path(rows, path) == 0) {
         w = 2 * current_cu_count() / gqa_head_blocks(hkv);
     } else {
-        const int hpb = 512 / d;  // heads per MFMA block; one block per CU (LDS ring)
-        w = current_cu_count() / ((hkv + hpb - 1) / hpb);
+        int hpb, per_cu;
+        gqa_mfma_geometry(d, hpb, per_cu);  // blocks stay resident through their LDS ring
+        w = per_cu * current_cu_count() / ((hkv + hpb - 1) / hpb);
     }
     if (w < 1) w = 1;
     const long max_tiles = (long)b * ((t_max + da::kGqaTile - 1) / da::kGqaTile);
@@ -170,18 +204,18 @@ hipError_t launch_gqa_mfma(const uint16_t *q, const uint16_t *k, const uint16_t 
                            da::PlanHeader *hdr, int *tile_start, int *slot_start, float *part_out, float *part_lse,
                            int workers, hipStream_t stream)
 {
-    using C = da::GqaMfmaCfg<D, RBLK>;
+    using C = GqaMfmaCfgFor<D, RBLK>;
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(attr_once, [] {
-        attr_err = hipFuncSetAttribute((const void *)da::gqa_mfma_kernel<D, RBLK>,
+        attr_err = hipFuncSetAttribute((const void *)da::gqa_mfma_kernel<D, RBLK, C::HPB, C::NST>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     });
     if (attr_err != hipSuccess) return attr_err;
     const int hb = (hkv + C::HPB - 1) / C::HPB;
     const int units = workers * hb;
     const int grid = (units + 7) / 8 * 8;
-    hipLaunchKernelGGL((da::gqa_mfma_kernel<D, RBLK>), dim3(grid), dim3(C::THREADS), C::LDS_BYTES, stream, q, k, v,
+    hipLaunchKernelGGL((da::gqa_mfma_kernel<D, RBLK, C::HPB, C::NST>), dim3(grid), dim3(C::THREADS), C::LDS_BYTES, stream, q, k, v,
                        seqlens, b, s, hq, hkv, t_max, scale_log2, hb, units, hdr, tile_start, slot_start, out, lse,
                        part_out, part_lse);
     return hipSuccess;

@@ -277,17 +277,38 @@ namespace da {
 // heads, d contiguous); 16-byte chunk c of token row t is stored at
 // c ^ gqa_swz(t), which keeps the score reads and the transposing reads free of
 // bank conflicts on 64 banks.
-template <int D, int RBLK>
+// Waits until at most `later` * LW copies of this wave are outstanding (`later`
+// runs from 0 to MAXL; the counter limit needs constants).
+template <int LW, int MAXL>
+__device__ __forceinline__ void wait_stage_copies(int later)
+{
+    if constexpr (MAXL > 0) {
+        if (later >= MAXL) {
+            wait_vmcnt<MAXL * LW>();
+            return;
+        }
+        wait_stage_copies<LW, MAXL - 1>(later);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
+template <int D, int RBLK, int HPB_ = 512 / D, int NST_ = 4>
 struct GqaMfmaCfg {
     static_assert(D == 64 || D == 128 || D == 256, "head dim");
-    static constexpr int HPB = 512 / D;          // KV heads (waves) per block
+    static constexpr int HPB = HPB_;             // KV heads (waves) per block
+    static_assert(HPB >= 1 && HPB * D <= 512, "token row of the block's heads fits 1 KB");
     static constexpr int THREADS = 64 * HPB;
     static constexpr int T = 16;                 // tokens per stage
-    static constexpr int ROWB = 1024;            // bytes of one token row (HPB heads x d)
+    static constexpr int ROWB = HPB * D * 2;     // bytes of one token row (HPB heads x d)
     static constexpr int STAGE_BYTES = 2 * T * ROWB;
-    static constexpr int NST = 4;                // ring depth
+    static constexpr int NST = NST_;             // ring depth (NST - 1 stages in flight)
     static constexpr int LDS_BYTES = NST * STAGE_BYTES;
-    static constexpr int LW = 2 * T / HPB;       // DMA instructions per wave per stage
+    static constexpr int RPC = 1024 / ROWB;      // token rows per 1 KB copy instruction
+    static constexpr int LPR = ROWB / 16;        // lanes per token row
+    static constexpr int LW = STAGE_BYTES / 1024 / HPB;  // copy instructions per wave per stage
+    static_assert(LW * HPB * 1024 == STAGE_BYTES, "stage splits into whole copies per wave");
+    static_assert((NST - 2) * LW <= 63, "outstanding copies fit the vmcnt counter");
     static constexpr int KS = D / 32;            // score k-steps
     static constexpr int DB = D / 16;            // 16-wide output blocks
 };
@@ -304,8 +325,8 @@ __device__ __forceinline__ int gqa_swz(int t)
 }
 
 
-template <int D, int RBLK>
-__global__ void __launch_bounds__(64 * (512 / D), 1)
+template <int D, int RBLK, int HPB, int NST>
+__global__ void __launch_bounds__(64 * HPB, 1)
     gqa_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
                     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens, int B, int s, int hq,
                     int hkv, int t_max, float scale_log2, int head_blocks, int units,
@@ -313,7 +334,7 @@ __global__ void __launch_bounds__(64 * (512 / D), 1)
                     const int *__restrict__ slot_start, uint16_t *__restrict__ out, float *__restrict__ lse,
                     float *__restrict__ part_out, float *__restrict__ part_lse)
 {
-    using C = GqaMfmaCfg<D, RBLK>;
+    using C = GqaMfmaCfg<D, RBLK, HPB, NST>;
     constexpr int SUB = kGqaTile / C::T;  // stages per planner tile
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     DA_LDS char *lds = (DA_LDS char *)smem;
@@ -349,12 +370,14 @@ __global__ void __launch_bounds__(64 * (512 / D), 1)
     const int hsel = (n & 3) >> 1;
     const int tr_base = (C::T + tr_tok) * C::ROWB + ((n & 1) << 3);
 
-    // ---- DMA of one stage: rows r = w, w + HPB, ... (0..15 K, 16..31 V)
+    // ---- DMA of one stage: 1 KB copies w, w + HPB, ... (token rows 0..15 K, 16..31 V)
     auto stage_pos = [&](int sg, int &bq, int &tok0) {
         const int tt = tile_lo + sg / SUB;
         bq = find_sequence(tile_start, B, tt);
         tok0 = (tt - tile_start[bq]) * kGqaTile + (sg % SUB) * C::T;
     };
+    const int lrow = lane / C::LPR;  // token row of this lane within a copy
+    const int lchk = lane % C::LPR;  // 16-byte chunk of this lane within its row
     auto issue_stage = [&](int sg) {
         int bq, tok0;
         stage_pos(sg, bq, tok0);
@@ -363,13 +386,14 @@ __global__ void __launch_bounds__(64 * (512 / D), 1)
         DA_LDS char *dst = lds + (sg % C::NST) * C::STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < C::LW; ++i) {
-            const int r = w + i * C::HPB;  // wave-uniform
-            const int tk = r & 15;
-            const uint16_t *base = (r < 16 ? kc : vc) + (size_t)bq * t_max * tok_elems;
+            const int cp = w + i * C::HPB;           // wave-uniform copy index
+            const int r = cp * C::RPC + lrow;        // K rows 0..T-1, V rows T..2T-1
+            const int tk = r & (C::T - 1);
+            const uint16_t *base = (cp * C::RPC < C::T ? kc : vc) + (size_t)bq * t_max * tok_elems;
             const u32x4 rsrc = raw_buffer_rsrc(base, (uint32_t)nrec);
-            const int c = lane ^ gqa_swz(tk);
+            const int c = lchk ^ gqa_swz(tk);
             const uint32_t off = (uint32_t)(((tok0 + tk) * (int)tok_elems + hb * C::HPB * D) * 2 + c * 16);
-            lds_dma16(rsrc, dst + r * C::ROWB, off);
+            lds_dma16(rsrc, dst + cp * 1024, off);
         }
     };
 
@@ -444,7 +468,7 @@ __global__ void __launch_bounds__(64 * (512 / D), 1)
     int te_cur = tile_start[bcur + 1];
     int L = clamp_len(seqlens[bcur], t_max);
     begin_segment(bcur);
-    for (int sg = 0; sg < min(3, nst); ++sg) issue_stage(sg);
+    for (int sg = 0; sg < min(C::NST - 1, nst); ++sg) issue_stage(sg);
 
     for (int sg = 0; sg < nst; ++sg) {
         const int tt = tile_lo + sg / SUB;
@@ -457,15 +481,9 @@ __global__ void __launch_bounds__(64 * (512 / D), 1)
             begin_segment(bcur);
         }
         // wait for this stage's copies (the later stages issued so far may stay in flight)
-        const int later = min(2, nst - 1 - sg);
-        if (later == 2)
-            wait_vmcnt<2 * C::LW>();
-        else if (later == 1)
-            wait_vmcnt<C::LW>();
-        else
-            wait_vmcnt<0>();
+        wait_stage_copies<C::LW, C::NST - 2>(min(C::NST - 2, nst - 1 - sg));
         lds_barrier();
-        if (sg + 3 < nst) issue_stage(sg + 3);
+        if (sg + C::NST - 1 < nst) issue_stage(sg + C::NST - 1);
 
         const int tok0 = (tt - ts_cur) * kGqaTile + (sg % SUB) * C::T;
         if (!active || tok0 >= L) continue;
