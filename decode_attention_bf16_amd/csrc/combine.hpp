@@ -10,6 +10,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "plan.hpp"
 
 namespace da {
 
@@ -17,12 +18,14 @@ namespace da {
 // over the 64 lanes. A launch of a few blocks per CU keeps the cost low when
 // most rows belong to single-segment sequences and are skipped.
 template <int DV>
-__global__ void __launch_bounds__(256) combine_kernel(int B, int M, const int *__restrict__ slot_start,
+__global__ void __launch_bounds__(256) combine_kernel(int B, int M, const PlanHeader *__restrict__ hdr,
+                                                      const int *__restrict__ slot_start,
                                                       const float *__restrict__ part_out,
                                                       const float *__restrict__ part_lse,
                                                       uint16_t *__restrict__ out, float *__restrict__ lse)
 {
     static_assert(DV % 64 == 0, "whole columns per lane");
+    if (hdr->merge_seqs == 0) return;  // every sequence was written by its one worker
     constexpr int CPL = DV / 64;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;

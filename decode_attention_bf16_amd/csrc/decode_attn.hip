@@ -104,7 +104,7 @@ hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint1
                        part_out, part_lse);
     const long rows = (long)b * s * h;
     hipLaunchKernelGGL(da::combine_kernel<K>, dim3(da::combine_grid(rows, current_cu_count())), dim3(256), 0, stream, b, s * h,
-                       slot_start, part_out, part_lse, out, lse);
+                       hdr, slot_start, part_out, part_lse, out, lse);
     return hipGetLastError();
 }
 
@@ -395,13 +395,13 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
     const long nrows = (long)b * s * hq;
     if (d == 64)
         hipLaunchKernelGGL(da::combine_kernel<64>, dim3(da::combine_grid(nrows, current_cu_count())), dim3(256), 0, st_, b, s * hq,
-                           slot_start, part_out, part_lse, out, lse);
+                           hdr, slot_start, part_out, part_lse, out, lse);
     else if (d == 128)
         hipLaunchKernelGGL(da::combine_kernel<128>, dim3(da::combine_grid(nrows, current_cu_count())), dim3(256), 0, st_, b, s * hq,
-                           slot_start, part_out, part_lse, out, lse);
+                           hdr, slot_start, part_out, part_lse, out, lse);
     else
         hipLaunchKernelGGL(da::combine_kernel<256>, dim3(da::combine_grid(nrows, current_cu_count())), dim3(256), 0, st_, b, s * hq,
-                           slot_start, part_out, part_lse, out, lse);
+                           hdr, slot_start, part_out, part_lse, out, lse);
     return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

@@ -20,6 +20,7 @@ struct PlanHeader {
     int per;  // tiles per worker (>= 1)
     int workers;
     int tile;
+    int merge_seqs;  // sequences the combine kernel must write (segments != 1)
 };
 
 // Workspace layout (all offsets 256-byte aligned), shared by MLA and GQA.
@@ -65,60 +66,80 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int &total)
     return incl - v;
 }
 
-// One wave. Lane l owns a contiguous run of ceil(b / 64) sequences.
+constexpr int kPlanRegChunks = 4;  // chunks of 64 sequences kept in registers between the passes
+
+// Segments of a sequence whose nt tiles start at flat tile `first`.
+__device__ __forceinline__ int plan_segments(int first, int nt, int per)
+{
+    return nt > 0 ? (first + nt - 1) / per - first / per + 1 : 0;
+}
+
+// One wave. Sequence i is lane i % 64 of chunk i / 64. The first
+// kPlanRegChunks chunks stay in registers from the first pass to the second,
+// so a batch of up to 256 sequences costs one dependent round trip to memory
+// (the seqlens loads); larger batches reload their later chunks.
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t *__restrict__ seqlens, int b, int t_max,
                                                             int tile, int workers, PlanHeader *__restrict__ hdr,
                                                             int *__restrict__ tile_start,
                                                             int *__restrict__ slot_start)
 {
     const int lane = threadIdx.x;
-    const int chunk = (b + kPlanThreads - 1) / kPlanThreads;
-    const int lo = min(b, lane * chunk);
-    const int hi = min(b, lo + chunk);
-
     // Pass 1: tiles per sequence -> tile_start (exclusive prefix), total.
-    int local = 0;
-    for (int i = lo; i < hi; ++i) {
-        const int L = clamp_len(seqlens[i], t_max);
-        local += (L + tile - 1) / tile;
+    int nt_r[kPlanRegChunks], first_r[kPlanRegChunks];
+#pragma unroll
+    for (int c = 0; c < kPlanRegChunks; ++c) {
+        const int i = c * kPlanThreads + lane;
+        const int L = i < b ? clamp_len(seqlens[i], t_max) : 0;
+        nt_r[c] = (L + tile - 1) / tile;
     }
-    int total = 0;
-    int run = wave_exclusive_scan(local, total);
-    for (int i = lo; i < hi; ++i) {
-        tile_start[i] = run;
-        const int L = clamp_len(seqlens[i], t_max);
-        run += (L + tile - 1) / tile;
+    int run = 0;
+#pragma unroll
+    for (int c = 0; c < kPlanRegChunks; ++c) {
+        int tot;
+        const int ex = wave_exclusive_scan(nt_r[c], tot);
+        first_r[c] = run + ex;
+        const int i = c * kPlanThreads + lane;
+        if (i < b) tile_start[i] = first_r[c];
+        run += tot;
     }
+    for (int base = kPlanRegChunks * kPlanThreads; base < b; base += kPlanThreads) {
+        const int i = base + lane;
+        const int L = i < b ? clamp_len(seqlens[i], t_max) : 0;
+        int tot;
+        const int ex = wave_exclusive_scan((L + tile - 1) / tile, tot);
+        if (i < b) tile_start[i] = run + ex;
+        run += tot;
+    }
+    const int total = run;
     const int per = max(1, (total + workers - 1) / workers);
 
-    // Pass 2: segments per sequence -> slot_start.
-    int segs = 0;
-    for (int i = lo; i < hi; ++i) {
-        const int L = clamp_len(seqlens[i], t_max);
-        const int nt = (L + tile - 1) / tile;
-        if (nt > 0) {
-            const int first = tile_start[i];
-            segs += (first + nt - 1) / per - first / per + 1;
-        }
-    }
-    int segs_total = 0;
-    int srun = wave_exclusive_scan(segs, segs_total);
-    for (int i = lo; i < hi; ++i) {
-        slot_start[i] = srun;
-        const int L = clamp_len(seqlens[i], t_max);
-        const int nt = (L + tile - 1) / tile;
-        if (nt > 0) {
-            const int first = tile_start[i];
-            srun += (first + nt - 1) / per - first / per + 1;
-        }
+    // Pass 2: segments per sequence -> slot_start; sequences to merge.
+    int srun = 0, nmerge = 0;
+    auto chunk2 = [&](int base, int nt, int first) {
+        const int i = base + lane;
+        const int segs = i < b ? plan_segments(first, nt, per) : 1;
+        int tot;
+        const int ex = wave_exclusive_scan(i < b ? segs : 0, tot);
+        if (i < b) slot_start[i] = srun + ex;
+        srun += tot;
+        nmerge += __builtin_popcountll(__builtin_amdgcn_ballot_w64(segs != 1));
+    };
+#pragma unroll
+    for (int c = 0; c < kPlanRegChunks; ++c)
+        if (c * kPlanThreads < b) chunk2(c * kPlanThreads, nt_r[c], first_r[c]);
+    for (int base = kPlanRegChunks * kPlanThreads; base < b; base += kPlanThreads) {
+        const int i = base + lane;
+        const int L = i < b ? clamp_len(seqlens[i], t_max) : 0;
+        chunk2(base, (L + tile - 1) / tile, i < b ? tile_start[i] : 0);
     }
     if (lane == 0) {
         tile_start[b] = total;
-        slot_start[b] = segs_total;
+        slot_start[b] = srun;
         hdr->total_tiles = total;
         hdr->per = per;
         hdr->workers = workers;
         hdr->tile = tile;
+        hdr->merge_seqs = nmerge;
     }
 }
 
