@@ -109,6 +109,24 @@ def test_mla_small(da, oracle_mod, case, workers):
     compare(out, lse, ref_o, ref_l, "mla %s w=%d" % (case, workers))
 
 
+def seeded_lengths(n, t_max, seed):
+    g = torch.Generator().manual_seed(seed)
+    sl = torch.randint(0, t_max + 1, (n,), generator=g).tolist()
+    sl[0], sl[1], sl[-1] = 0, t_max, 1  # an empty, a full and a one-row sequence
+    return sl
+
+
+@pytest.mark.parametrize("workers", [0, 7, 1000])
+def test_mla_many_sequences(da, oracle_mod, workers):
+    """More sequences than the planner keeps in registers (256): its later chunks take the reload path."""
+    shape = mla_shape(300, 1, 16, 64, 16, 70, seed=31)
+    tensors = wl.make_mla(shape, seqlens=seeded_lengths(300, 70, 5))
+    print("mla many sequences workers", workers, flush=True)
+    out, lse = run_mla(da, shape, tensors, workers)
+    ref_o, ref_l = oracle_mod.mla(*tensors, shape.scale)
+    compare(out, lse, ref_o, ref_l, "mla b=300 w=%d" % workers)
+
+
 def test_mla_split_counts_agree(da):
     shape = mla_shape(4, 2, 64, 512, 64, 700, seed=7)
     tensors = wl.make_mla(shape, seqlens=[700, 511, 65, 300])
@@ -215,6 +233,8 @@ GQA_SMALL = [
     (2, 8, 64, 8, 64, 100, [100, 9]),       # 64 rows per KV head, d = 64
     (3, 1, 64, 8, 128, 520, [520, 1, 257]),  # the layer's geometry, ragged
     (1, 4, 32, 4, 256, 64, [64]),            # d = 256, 32 rows
+    (2, 1, 10, 5, 128, 90, [90, 40]),        # 5 KV heads: the second head block has one active wave
+    (2, 2, 18, 9, 64, 80, [80, 3]),          # d = 64, 9 KV heads over two head blocks
 ]
 
 
@@ -234,6 +254,18 @@ def test_gqa_small(da, oracle_mod, case, path, workers):
     out, lse = run_gqa(da, shape, tensors, workers, path)
     ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale)
     compare(out, lse, ref_o, ref_l, "gqa %s path=%d w=%d" % (case, path, workers))
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("workers", [0, 3])
+def test_gqa_many_sequences(da, oracle_mod, path, workers):
+    """More sequences than the planner keeps in registers (256)."""
+    shape = wl.GQAShape(b=300, s=1, hq=8, hkv=2, d=64, t_max=40, scale=0.125, seed=32)
+    tensors = wl.make_gqa(shape, seqlens=seeded_lengths(300, 40, 6))
+    print("gqa many sequences path", path, "workers", workers, flush=True)
+    out, lse = run_gqa(da, shape, tensors, workers, path)
+    ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale)
+    compare(out, lse, ref_o, ref_l, "gqa b=300 path=%d w=%d" % (path, workers))
 
 
 @pytest.mark.parametrize("path", [1, 2])
