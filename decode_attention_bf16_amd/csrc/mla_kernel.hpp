@@ -8,21 +8,23 @@
 // s*h query rows of a sequence are the M dimension of two dense contractions
 // (scores and values) against one shared [tokens, k+p] tile.
 //
-// Work decomposition: a block (512 threads, 8 waves, two per SIMD) is one
-// worker of the split-KV plan times one block of 64 query rows. The waves have
-// two roles and form a two-stage software pipeline over 32-token tiles:
+// Work decomposition: a block (4 score waves plus NVW = 8 value waves, three
+// waves per SIMD, when k >= 256; 4 + 4 otherwise) is one worker of the
+// split-KV plan times one block of 64 query rows. The waves have two roles and
+// form a two-stage software pipeline over 32-token tiles:
 //   score waves (0..3), 16 rows each: S^T[32 tokens, 16 rows] = tile . Q^T with
 //     MFMA 16x16x32 bf16 (A = cache tile from LDS, B = the rows' queries held
 //     in registers), then the fp32 online softmax of those rows (exp2 domain,
 //     lazily moved reference maximum). They publish the bf16 probabilities in
 //     the value product's operand layout, the per-row rescale factors when the
 //     reference moved and, at the end of a segment, each row's (max, sum).
-//   value waves (4..7), all 64 rows x k/4 latent columns each: O^T += V^T . P^T
-//     with MFMA 16x16x32, A = latent columns of the same LDS tile through the
-//     transposing LDS read (ds_read_b64_tr_b16), B = the published
-//     probabilities; every A fragment feeds four row blocks. They also copy the
-//     cache tiles HBM -> LDS (buffer_load ... lds, 16 bytes per lane, no
-//     registers) two tiles ahead, and write the outputs.
+//   value waves (4 .. 3+NVW), all 64 rows x k/NVW latent columns each:
+//     O^T += V^T . P^T with MFMA 32x32x16 bf16 when those columns fill 32-wide
+//     blocks (16x16x32 otherwise), A = latent columns of the same LDS tile
+//     through the transposing LDS read (ds_read_b64_tr_b16), B = the published
+//     probabilities. The first four also copy the cache tiles HBM -> LDS
+//     (buffer_load ... lds, 16 bytes per lane, no registers) two tiles ahead;
+//     all write their columns of the outputs.
 // In step j the score waves work on tile j while the value waves work on tile
 // j-1, so on every SIMD one wave's softmax and LDS traffic overlap the other's
 // matrix work, and the score waves never wait for HBM. One barrier per step;
@@ -58,15 +60,17 @@ struct MlaCfg {
     static constexpr int T = kMlaTile;
     static constexpr int TILE_BYTES = T * ROW_BYTES;
     static constexpr int NBUF = 4;
-    static constexpr int THREADS = 512;
+    // value waves: eight when k >= 256 (each owns k/8 latent columns), else four
+    static constexpr int NVW = K >= 256 ? 8 : 4;
+    static constexpr int THREADS = 64 * (4 + NVW);
     static constexpr int ROWS = kMlaRows;
     static constexpr int LPW = T * ROW_CHUNKS / 256;            // copy instructions per value wave per tile
     static_assert(T * ROW_CHUNKS % 256 == 0, "tile chunks divisible among the four copying waves");
-    static constexpr int CBV = K / 64;                          // 16-column output blocks per value wave
+    static constexpr int CBV = K / (16 * NVW);                  // 16-column output blocks per value wave
     // value product with v_mfma_f32_32x32x16_bf16 (two chained 16-token k-steps
     // per accumulator and tile) when a value wave's columns fill 32-column blocks
-    static constexpr bool WIDE = K % 128 == 0;
-    static constexpr int CB32 = K / 128;                        // 32-column output blocks per value wave
+    static constexpr bool WIDE = K % (32 * NVW) == 0;
+    static constexpr int CB32 = K / (32 * NVW);                 // 32-column output blocks per value wave
     static constexpr int QCH = 3;                               // score k-steps per LDS read chunk
     static constexpr int PBUF_OFF = NBUF * TILE_BYTES;          // [2 slots][4 row blocks][64 lanes] x 16 B
     static constexpr int ALPHA_OFF = PBUF_OFF + 2 * 4 * 64 * 16;  // [2 slots][64 rows] float
@@ -110,7 +114,7 @@ struct SeqCursor {
 };
 
 template <int K, int P>
-__global__ void __launch_bounds__(512, 1)
+__global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
     mla_decode_kernel(const uint16_t *__restrict__ q_lat, const uint16_t *__restrict__ q_rope,
                       const uint16_t *__restrict__ cache, const int32_t *__restrict__ seqlens, int B, int s,
                       int h, int t_max, float scale_log2, int row_blocks, int units,
@@ -305,10 +309,10 @@ __global__ void __launch_bounds__(512, 1)
         for (int jj = 0; jj < 4; ++jj) tr_off[jj] = tr_row + (((2 * jj + hsel) ^ st) << 4);
         // byte offset (within a tile) of this lane's read for output column block cb
         auto tr_addr = [&](int cb) -> int {
-            if constexpr (K % 256 == 0) {
-                return tr_off[cb & 3] + 128 * (vw * (K / 256) + (cb >> 2));
+            if constexpr (C::CBV % 4 == 0) {
+                return tr_off[cb & 3] + 128 * (vw * (C::CBV / 4) + (cb >> 2));
             } else {
-                const int jj = vw * (K / 64) + cb;  // 16-column block across the full latent width
+                const int jj = vw * C::CBV + cb;  // 16-column block across the full latent width
                 return tr_row + (((2 * (jj & 3) + hsel) ^ st) << 4) + 128 * (jj >> 2);
             }
         };
@@ -373,21 +377,25 @@ __global__ void __launch_bounds__(512, 1)
         // of column 32cb + l%32 of this wave's columns
         auto tr32_addr = [&](int cb, int ks, int h) -> int {
             const int tok = 16 * ks + 8 * (g >> 1) + 4 * h + (n >> 2);
-            const int chunk = (vw * (K / 4) + 32 * cb) / 8 + 2 * (g & 1) + ((n >> 1) & 1);
+            const int chunk = (vw * (K / C::NVW) + 32 * cb) / 8 + 2 * (g & 1) + ((n >> 1) & 1);
             return tok * C::ROW_BYTES + (((chunk & ~7) | ((chunk ^ tile_swz(tok)) & 7)) << 4) + ((n & 1) << 3);
         };
         SeqCursor cur;
 
-        issue_tile(0);
-        if (ntiles > 1) {
-            issue_tile(1);
-            wait_vmcnt<C::LPW>();
-        } else {
-            wait_vmcnt<0>();
+        // the first four value waves copy the tiles (LPW copies each per tile)
+        const bool copier = vw < 4;
+        if (copier) {
+            issue_tile(0);
+            if (ntiles > 1) {
+                issue_tile(1);
+                wait_vmcnt<C::LPW>();
+            } else {
+                wait_vmcnt<0>();
+            }
         }
         lds_barrier();  // tile 0 has landed
         for (int j = 0; j <= ntiles; ++j) {
-            const bool issued = j + 2 < ntiles;
+            const bool issued = copier && j + 2 < ntiles;
             bool stored = false;
             const int tt = tile_lo + j - 1;
             const int slot = (j - 1) & 1;
@@ -530,7 +538,7 @@ __global__ void __launch_bounds__(512, 1)
                             if (row < M) {
                                 float inv, lse2;
                                 row_info(rloc, inv, lse2);
-                                const int col0 = vw * (K / 4) + 4 * (g >> 1);
+                                const int col0 = vw * (K / C::NVW) + 4 * (g >> 1);
 #pragma unroll
                                 for (int cb = 0; cb < C::CB32; ++cb)
 #pragma unroll
@@ -550,7 +558,7 @@ __global__ void __launch_bounds__(512, 1)
                             if (row < M) {
                                 float inv, lse2;
                                 row_info(rloc, inv, lse2);
-                                const int col0 = vw * (K / 4) + g * 4;
+                                const int col0 = vw * (K / C::NVW) + g * 4;
 #pragma unroll
                                 for (int cb = 0; cb < C::CBV; ++cb) put4(row, col0 + 16 * cb, acc[r4][cb], inv);
                                 put_lse(row, lse2);
@@ -561,7 +569,7 @@ __global__ void __launch_bounds__(512, 1)
                 }
             }
             // tile j+1 (issued a step ago) must be in LDS before the barrier publishes it
-            if (j + 1 < ntiles) {
+            if (copier && j + 1 < ntiles) {
                 if (issued && !stored)
                     wait_vmcnt<C::LPW>();
                 else
