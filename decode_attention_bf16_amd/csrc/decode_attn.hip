@@ -91,8 +91,6 @@ hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint1
     float *part_lse = (float *)(wsp + ws.part_lse);
     float *part_out = (float *)(wsp + ws.part_out);
 
-    hipLaunchKernelGGL(da::plan_kernel, dim3(1), dim3(da::kPlanThreads), 0, stream, seqlens, b, t_max, C::T, workers,
-                       hdr, tile_start, slot_start);
     const int rb = mla_row_blocks(s, h);
     const int units = workers * rb;
     const int grid = (units + 7) / 8 * 8;
@@ -363,8 +361,6 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
     hipStream_t st_ = (hipStream_t)stream;
     const float sl2 = scale * da::kLog2e;
 
-    hipLaunchKernelGGL(da::plan_kernel, dim3(1), dim3(da::kPlanThreads), 0, st_, seqlens, b, t_max, da::kGqaTile,
-                       workers, hdr, tile_start, slot_start);
     if (log_plan())
         fprintf(stderr, "[decode_attn] gqa d=%d b=%d s=%d hq=%d hkv=%d t_max=%d workers=%d path=%s\n", d, b, s, hq,
                 hkv, t_max, workers, use_mfma ? "mfma" : "valu");

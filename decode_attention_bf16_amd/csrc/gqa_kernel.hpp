@@ -39,8 +39,8 @@ __global__ void __launch_bounds__(256)
     gqa_valu_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
                     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens, int B, int s, int hq,
                     int hkv, int t_max, float scale_log2, int head_blocks, int units,
-                    const PlanHeader *__restrict__ hdr, const int *__restrict__ tile_start,
-                    const int *__restrict__ slot_start, uint16_t *__restrict__ out, float *__restrict__ lse,
+                    PlanHeader *__restrict__ hdr, int *__restrict__ tile_start,
+                    int *__restrict__ slot_start, uint16_t *__restrict__ out, float *__restrict__ lse,
                     float *__restrict__ part_out, float *__restrict__ part_lse)
 {
     using C = GqaValuCfg<D, R>;
@@ -51,13 +51,14 @@ __global__ void __launch_bounds__(256)
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int kvh = hb * 4 + wave;
+    // the plan as arrays for the combine kernel; every wave derives its own view
+    if (unit == 0 && wave == 0) write_plan(seqlens, B, t_max, kGqaTile, units / head_blocks, hdr, tile_start, slot_start);
     if (kvh >= hkv) return;
 
-    const int total = hdr->total_tiles;
-    const int per = hdr->per;
-    const int tile_lo = worker * per;
-    if (tile_lo >= total) return;
-    const int tile_hi = min(total, tile_lo + per);
+    PlanWalk cur;
+    if (!cur.init(seqlens, B, t_max, kGqaTile, units / head_blocks, worker)) return;
+    const int tile_lo = cur.tile_lo;
+    const int tile_hi = cur.tile_hi;
 
     const int dg = lane % C::LPT;
     const int slot = lane / C::LPT;
@@ -121,9 +122,9 @@ __global__ void __launch_bounds__(256)
             l[r] = lr;
         }
         if (slot != 0) return;
-        const int nseg = slot_start[bq + 1] - slot_start[bq];
+        const int nseg = cur.ns;
         const bool direct = nseg == 1;
-        const int sl = slot_start[bq] + (worker - first_tile_of_seq / per);
+        const int sl = cur.slot(worker);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             if (r >= Rr) continue;
@@ -147,18 +148,19 @@ __global__ void __launch_bounds__(256)
         }
     };
 
-    int bcur = find_sequence(tile_start, B, tile_lo);
-    int ts_cur = tile_start[bcur];
-    int te_cur = tile_start[bcur + 1];
+    int bcur = cur.b;
+    int ts_cur = cur.ts;
+    int te_cur = cur.te;
     int L = clamp_len(seqlens[bcur], t_max);
     begin_segment(bcur);
 
     for (int tt = tile_lo; tt < tile_hi; ++tt) {
         if (tt >= te_cur) {
             end_segment(bcur, ts_cur);
-            bcur = find_sequence(tile_start, B, tt);
-            ts_cur = tile_start[bcur];
-            te_cur = tile_start[bcur + 1];
+            cur.seek(seqlens, tt);
+            bcur = cur.b;
+            ts_cur = cur.ts;
+            te_cur = cur.te;
             L = clamp_len(seqlens[bcur], t_max);
             begin_segment(bcur);
         }
@@ -330,8 +332,8 @@ __global__ void __launch_bounds__(64 * HPB, 1)
     gqa_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
                     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens, int B, int s, int hq,
                     int hkv, int t_max, float scale_log2, int head_blocks, int units,
-                    const PlanHeader *__restrict__ hdr, const int *__restrict__ tile_start,
-                    const int *__restrict__ slot_start, uint16_t *__restrict__ out, float *__restrict__ lse,
+                    PlanHeader *__restrict__ hdr, int *__restrict__ tile_start,
+                    int *__restrict__ slot_start, uint16_t *__restrict__ out, float *__restrict__ lse,
                     float *__restrict__ part_out, float *__restrict__ part_lse)
 {
     using C = GqaMfmaCfg<D, RBLK, HPB, NST>;
@@ -343,11 +345,13 @@ __global__ void __launch_bounds__(64 * HPB, 1)
     if (unit >= units) return;
     const int worker = unit / head_blocks;
     const int hb = unit - worker * head_blocks;
-    const int total = hdr->total_tiles;
-    const int per = hdr->per;
-    const int tile_lo = worker * per;
-    if (tile_lo >= total) return;
-    const int tile_hi = min(total, tile_lo + per);
+    // the plan as arrays for the combine kernel; every wave derives its own view
+    if (unit == 0 && threadIdx.x < 64)
+        write_plan(seqlens, B, t_max, kGqaTile, units / head_blocks, hdr, tile_start, slot_start);
+    PlanWalk cur;
+    if (!cur.init(seqlens, B, t_max, kGqaTile, units / head_blocks, worker)) return;
+    const int tile_lo = cur.tile_lo;
+    const int tile_hi = cur.tile_hi;
     const int nst = (tile_hi - tile_lo) * SUB;
 
     const int tid = threadIdx.x;
@@ -371,10 +375,12 @@ __global__ void __launch_bounds__(64 * HPB, 1)
     const int tr_base = (C::T + tr_tok) * C::ROWB + ((n & 1) << 3);
 
     // ---- DMA of one stage: 1 KB copies w, w + HPB, ... (token rows 0..15 K, 16..31 V)
+    PlanWalk icur = cur;  // the copies' own cursor, ahead of the compute's
     auto stage_pos = [&](int sg, int &bq, int &tok0) {
         const int tt = tile_lo + sg / SUB;
-        bq = find_sequence(tile_start, B, tt);
-        tok0 = (tt - tile_start[bq]) * kGqaTile + (sg % SUB) * C::T;
+        icur.seek(seqlens, tt);
+        bq = icur.b;
+        tok0 = (tt - icur.ts) * kGqaTile + (sg % SUB) * C::T;
     };
     const int lrow = lane / C::LPR;  // token row of this lane within a copy
     const int lchk = lane % C::LPR;  // 16-byte chunk of this lane within its row
@@ -434,8 +440,8 @@ __global__ void __launch_bounds__(64 * HPB, 1)
     };
     auto end_segment = [&](int bq, int first_tile_of_seq) {
         if (!active) return;
-        const int nseg = slot_start[bq + 1] - slot_start[bq];
-        const int sl = slot_start[bq] + (worker - first_tile_of_seq / per);
+        const int nseg = cur.ns;
+        const int sl = cur.slot(worker);
 #pragma unroll
         for (int rb = 0; rb < RBLK; ++rb) {
             const int r = rb * 16 + n;
@@ -463,9 +469,9 @@ __global__ void __launch_bounds__(64 * HPB, 1)
     };
 
     // ---- prologue (queries first: their wait then drains nothing else)
-    int bcur = find_sequence(tile_start, B, tile_lo);
-    int ts_cur = tile_start[bcur];
-    int te_cur = tile_start[bcur + 1];
+    int bcur = cur.b;
+    int ts_cur = cur.ts;
+    int te_cur = cur.te;
     int L = clamp_len(seqlens[bcur], t_max);
     begin_segment(bcur);
     for (int sg = 0; sg < min(C::NST - 1, nst); ++sg) issue_stage(sg);
@@ -474,9 +480,10 @@ __global__ void __launch_bounds__(64 * HPB, 1)
         const int tt = tile_lo + sg / SUB;
         if (tt >= te_cur) {  // first stage of a new sequence (stage sg % SUB == 0)
             end_segment(bcur, ts_cur);
-            bcur = find_sequence(tile_start, B, tt);
-            ts_cur = tile_start[bcur];
-            te_cur = tile_start[bcur + 1];
+            cur.seek(seqlens, tt);
+            bcur = cur.b;
+            ts_cur = cur.ts;
+            te_cur = cur.te;
             L = clamp_len(seqlens[bcur], t_max);
             begin_segment(bcur);
         }

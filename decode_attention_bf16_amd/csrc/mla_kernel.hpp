@@ -98,29 +98,14 @@ __device__ __forceinline__ int tile_swz(int r)
     return (i0 ^ i2) | (i0 << 1) | ((i1 ^ i2) << 2);
 }
 
-// Tile -> (sequence, its first tile, the first tile past it), cached while the
-// tiles stay inside one sequence. All values are wave-uniform.
-struct SeqCursor {
-    int b = -1, ts = 0, te = 0;
-    __device__ __forceinline__ void seek(const int *__restrict__ tile_start, int B, int tt)
-    {
-        if (b < 0 || tt >= te || tt < ts) {
-            b = find_sequence(tile_start, B, tt);
-            ts = tile_start[b];
-            te = tile_start[b + 1];
-            wait_lgkm_visible();
-        }
-    }
-};
-
 template <int K, int P>
 __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
     mla_decode_kernel(const uint16_t *__restrict__ q_lat, const uint16_t *__restrict__ q_rope,
                       const uint16_t *__restrict__ cache, const int32_t *__restrict__ seqlens, int B, int s,
                       int h, int t_max, float scale_log2, int row_blocks, int units,
-                      const PlanHeader *__restrict__ hdr, const int *__restrict__ tile_start,
-                      const int *__restrict__ slot_start, uint16_t *__restrict__ out, float *__restrict__ lse,
-                      float *__restrict__ part_out, float *__restrict__ part_lse)
+                      PlanHeader *__restrict__ hdr, int *__restrict__ tile_start, int *__restrict__ slot_start,
+                      uint16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ part_out,
+                      float *__restrict__ part_lse)
 {
     using C = MlaCfg<K, P>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -131,11 +116,14 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
     if (unit >= units) return;
     const int worker = unit / row_blocks;
     const int rb = unit - worker * row_blocks;
-    const int total = hdr->total_tiles;
-    const int per = hdr->per;
-    const int tile_lo = worker * per;
-    if (tile_lo >= total) return;
-    const int ntiles = min(total, tile_lo + per) - tile_lo;
+    const int workers = units / row_blocks;
+    // the plan as arrays for the combine kernel; every wave derives its own view
+    if (unit == 0 && threadIdx.x < 64) write_plan(seqlens, B, t_max, C::T, workers, hdr, tile_start, slot_start);
+    PlanWalk plan;
+    if (!plan.init(seqlens, B, t_max, C::T, workers, worker)) return;
+    const int per = plan.per;
+    const int tile_lo = plan.tile_lo;
+    const int ntiles = plan.tile_hi - tile_lo;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -161,14 +149,14 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
         bf16x8 qB[C::KSTEPS];
         float mref = -INFINITY, lsum = 0.f;
         int nvis = 0, nvis_min = 0;
-        SeqCursor cur;
+        PlanWalk cur = plan;
 
         lds_barrier();  // tile 0 has landed
         for (int j = 0; j <= ntiles; ++j) {
             if (j < ntiles) {
                 const int tt = tile_lo + j;
-                const bool new_seg = cur.b < 0 || tt >= cur.te;
-                cur.seek(tile_start, B, tt);
+                const bool new_seg = j == 0 || tt >= cur.te;
+                cur.seek(seqlens, tt);
                 if (new_seg) {
                     const int L = clamp_len(seqlens[cur.b], t_max);
                     nvis = row_ok ? (L - s + row / h + 1) : 0;
@@ -320,11 +308,11 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
         // HBM -> LDS copy of tile j of this worker into buffer j % NBUF:
         // copy_setup resolves the sequence, copy_part issues copy instruction
         // `it` of this wave (LPW per wave per tile).
-        SeqCursor dma;
+        PlanWalk dma = plan;
         int dma_b = -1, dma_len = 0;
         auto copy_setup = [&](int j, u32x4 &rsrc, uint32_t &tile_bytes_in_seq) {
             const int tt = tile_lo + j;
-            dma.seek(tile_start, B, tt);
+            dma.seek(seqlens, tt);
             if (dma.b != dma_b) {
                 dma_b = dma.b;
                 dma_len = clamp_len(seqlens[dma.b], t_max);
@@ -380,7 +368,7 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
             const int chunk = (vw * (K / C::NVW) + 32 * cb) / 8 + 2 * (g & 1) + ((n >> 1) & 1);
             return tok * C::ROW_BYTES + (((chunk & ~7) | ((chunk ^ tile_swz(tok)) & 7)) << 4) + ((n & 1) << 3);
         };
-        SeqCursor cur;
+        PlanWalk cur = plan;
 
         // the first four value waves copy the tiles (LPW copies each per tile)
         const bool copier = vw < 4;
@@ -440,8 +428,8 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
             }
             __builtin_amdgcn_sched_barrier(0);
             if (j >= 1) {
-                const bool new_seg = cur.b < 0 || tt >= cur.te;
-                cur.seek(tile_start, B, tt);
+                const bool new_seg = j == 1 || tt >= cur.te;
+                cur.seek(seqlens, tt);
                 if (new_seg) zero_acc();
                 // rows whose reference maximum moved: bring the sums to the new reference
                 if (__builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3])) {
@@ -502,8 +490,8 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
                 // end of a segment: normalize and write the result or the partial
                 if (tt + 1 >= cur.te || j == ntiles) {
                     const int bq = cur.b;
-                    const int nseg = slot_start[bq + 1] - slot_start[bq];
-                    const int sl = slot_start[bq] + (worker - cur.ts / per);
+                    const int nseg = cur.ns;
+                    const int sl = cur.slot(worker);
                     // normalization of query row rloc (row of the block) and its output place
                     auto row_info = [&](int rloc, float &inv, float &lse2) {
                         const float mr = seg_buf[(slot * 64 + rloc) * 2 + 0];

@@ -9,6 +9,12 @@
 // slot_start[b] .. slot_start[b+1]-1. A sequence with exactly one segment is
 // finished by its worker; one with several is merged by the combine kernel.
 // The total number of segments is at most b + workers - 1.
+//
+// The plan costs no launch of its own: every wave of a tile kernel derives the
+// part it needs (PlanWalk: totals by a wave scan over seqlens, then a cursor
+// walking forward through its worker's sequences), and one wave of the tile
+// kernel's first block writes the whole plan as arrays for the combine kernel
+// that follows on the stream (write_plan).
 #pragma once
 
 #include "common.hpp"
@@ -74,16 +80,17 @@ __device__ __forceinline__ int plan_segments(int first, int nt, int per)
     return nt > 0 ? (first + nt - 1) / per - first / per + 1 : 0;
 }
 
-// One wave. Sequence i is lane i % 64 of chunk i / 64. The first
-// kPlanRegChunks chunks stay in registers from the first pass to the second,
-// so a batch of up to 256 sequences costs one dependent round trip to memory
-// (the seqlens loads); larger batches reload their later chunks.
-__global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t *__restrict__ seqlens, int b, int t_max,
-                                                            int tile, int workers, PlanHeader *__restrict__ hdr,
-                                                            int *__restrict__ tile_start,
-                                                            int *__restrict__ slot_start)
+// The whole plan as arrays (tile_start, slot_start, header) for the combine
+// kernel, written by one wave of the tile kernel. Sequence i is lane i % 64 of
+// chunk i / 64; the first kPlanRegChunks chunks stay in registers from the
+// first pass to the second, so a batch of up to 256 sequences costs one
+// dependent round trip to memory (the seqlens loads); larger batches reload
+// their later chunks.
+__device__ __noinline__ void write_plan(const int32_t *__restrict__ seqlens, int b, int t_max, int tile, int workers,
+                                        PlanHeader *__restrict__ hdr, int *__restrict__ tile_start,
+                                        int *__restrict__ slot_start)
 {
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     // Pass 1: tiles per sequence -> tile_start (exclusive prefix), total.
     int nt_r[kPlanRegChunks], first_r[kPlanRegChunks];
 #pragma unroll
@@ -143,18 +150,101 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t *__res
     }
 }
 
-// Largest index i in [0, b] with tile_start[i] <= t (tile_start[b] = total).
-__device__ __forceinline__ int find_sequence(const int *__restrict__ tile_start, int b, int t)
-{
-    int lo = 0, hi = b;  // invariant: tile_start[lo] <= t
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (tile_start[mid] <= t)
-            lo = mid;
-        else
-            hi = mid - 1;
+
+// A wave's own view of the plan, computed from seqlens with no global scratch
+// and no other wave: the total tile count, `per`, this worker's tile range and
+// a cursor over the sequences of that range. For the cursor's sequence b it
+// holds b's tiles [ts, te), the first partial slot of b (ss = segments of all
+// sequences before b) and b's segment count ns. Every member is wave-uniform.
+struct PlanWalk {
+    int total = 0, per = 1, tile_lo = 0, tile_hi = 0;
+    int b = 0, ts = 0, te = 0, ss = 0, ns = 0;
+    int nb = 0, tmax = 0, tile = 1;
+
+    // Returns false when the worker has no tile (then nothing else is set).
+    __device__ bool init(const int32_t *__restrict__ seqlens, int B, int t_max, int tile_, int workers, int worker)
+    {
+        nb = B;
+        tmax = t_max;
+        tile = tile_;
+        const int lane = threadIdx.x & 63;
+        int nt_r[kPlanRegChunks];
+        int run = 0;
+#pragma unroll
+        for (int c = 0; c < kPlanRegChunks; ++c) {
+            const int i = c * kPlanThreads + lane;
+            const int L = i < B ? clamp_len(seqlens[i], t_max) : 0;
+            nt_r[c] = (L + tile - 1) / tile;
+        }
+#pragma unroll
+        for (int c = 0; c < kPlanRegChunks; ++c) {
+            int tot;
+            wave_exclusive_scan(nt_r[c], tot);
+            run += __builtin_amdgcn_readfirstlane(tot);
+        }
+        for (int base = kPlanRegChunks * kPlanThreads; base < B; base += kPlanThreads) {
+            const int i = base + lane;
+            const int L = i < B ? clamp_len(seqlens[i], t_max) : 0;
+            int tot;
+            wave_exclusive_scan((L + tile - 1) / tile, tot);
+            run += __builtin_amdgcn_readfirstlane(tot);
+        }
+        total = run;
+        per = max(1, (total + workers - 1) / workers);
+        tile_lo = worker * per;
+        if (tile_lo >= total) return false;
+        tile_hi = min(total, tile_lo + per);
+
+        // the sequence holding tile_lo, and the slots of the sequences before it
+        int run_t = 0, run_s = 0;
+        auto chunk = [&](int base, int nt) -> bool {
+            const int i = base + lane;
+            int t_tot, s_tot;
+            const int first = run_t + wave_exclusive_scan(nt, t_tot);
+            const int seg = i < B ? plan_segments(first, nt, per) : 0;
+            const int sfirst = run_s + wave_exclusive_scan(seg, s_tot);
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(nt > 0 && first <= tile_lo && tile_lo < first + nt);
+            if (hit) {
+                const int l = (int)__builtin_ctzll(hit);
+                b = base + l;
+                ts = __builtin_amdgcn_readlane(first, l);
+                te = ts + __builtin_amdgcn_readlane(nt, l);
+                ss = __builtin_amdgcn_readlane(sfirst, l);
+                ns = __builtin_amdgcn_readlane(seg, l);
+                return true;
+            }
+            run_t += __builtin_amdgcn_readfirstlane(t_tot);
+            run_s += __builtin_amdgcn_readfirstlane(s_tot);
+            return false;
+        };
+#pragma unroll
+        for (int c = 0; c < kPlanRegChunks; ++c)
+            if (c * kPlanThreads < B && chunk(c * kPlanThreads, nt_r[c])) return true;
+        for (int base = kPlanRegChunks * kPlanThreads; base < B; base += kPlanThreads) {
+            const int i = base + lane;
+            const int L = i < B ? clamp_len(seqlens[i], t_max) : 0;
+            if (chunk(base, (L + tile - 1) / tile)) return true;
+        }
+        return true;  // not reached: some sequence holds tile_lo < total
     }
-    return lo;
-}
+
+    // Moves the cursor forward to the sequence holding tile tt (tt >= ts).
+    __device__ __forceinline__ void seek(const int32_t *__restrict__ seqlens, int tt)
+    {
+        if (tt < te) return;
+        do {
+            ss += ns;
+            ++b;
+            const int nt = (clamp_len(seqlens[b], tmax) + tile - 1) / tile;
+            ts = te;
+            te = ts + nt;
+            ns = plan_segments(ts, nt, per);
+        } while (tt >= te);
+        wait_lgkm_visible();
+    }
+
+    // Slot of this worker's segment of the cursor's sequence.
+    __device__ __forceinline__ int slot(int worker) const { return ss + (worker - ts / per); }
+};
 
 }  // namespace da
