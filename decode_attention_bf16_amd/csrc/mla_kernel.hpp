@@ -121,7 +121,6 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
     if (unit == 0 && threadIdx.x < 64) write_plan(seqlens, B, t_max, C::T, workers, hdr, tile_start, slot_start);
     PlanWalk plan;
     if (!plan.init(seqlens, B, t_max, C::T, workers, worker)) return;
-    const int per = plan.per;
     const int tile_lo = plan.tile_lo;
     const int ntiles = plan.tile_hi - tile_lo;
 
