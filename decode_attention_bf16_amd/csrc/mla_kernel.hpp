@@ -71,7 +71,8 @@ struct MlaCfg {
     // per accumulator and tile) when a value wave's columns fill 32-column blocks
     static constexpr bool WIDE = K % (32 * NVW) == 0;
     static constexpr int CB32 = K / (32 * NVW);                 // 32-column output blocks per value wave
-    static constexpr int QCH = 3;                               // score k-steps per LDS read chunk
+    static constexpr int QCH = 2;                               // score k-steps per LDS read chunk
+    static constexpr int QPF = 2;                               // chunks in flight ahead of the MFMAs
     static constexpr int PBUF_OFF = NBUF * TILE_BYTES;          // [2 slots][4 row blocks][64 lanes] x 16 B
     static constexpr int ALPHA_OFF = PBUF_OFF + 2 * 4 * 64 * 16;  // [2 slots][64 rows] float
     static constexpr int FLAG_OFF = ALPHA_OFF + 2 * 64 * 4;       // [2 slots][4 row blocks] int
@@ -180,16 +181,16 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
                 const DA_LDS char *tile = lds + (j % C::NBUF) * C::TILE_BYTES;
 
                 // S^T[32 tokens, 16 rows]. The tile's A fragments are read in
-                // chunks of QCH k-steps, two chunks ahead of the MFMAs that use
+                // chunks of QCH k-steps, QPF chunks ahead of the MFMAs that use
                 // them, so LDS latency hides behind matrix work. Each 16-token
                 // block accumulates in one chain: back-to-back MFMAs on the same
                 // accumulator forward it without a register read, which measured
                 // faster than spreading the k-steps over more accumulators.
                 f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
                 {
-                    constexpr int QCH = C::QCH;
+                    constexpr int QCH = C::QCH, QPF = C::QPF;
                     constexpr int NQC = (C::KSTEPS + QCH - 1) / QCH;
-                    bf16x8 af[2][2 * QCH];
+                    bf16x8 af[QPF][2 * QCH];
                     auto load_chunk = [&](int c, bf16x8(&d)[2 * QCH]) {
 #pragma unroll
                         for (int i = 0; i < QCH; ++i) {
@@ -201,8 +202,9 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
                             }
                         }
                     };
-                    load_chunk(0, af[0]);
-                    if (NQC > 1) load_chunk(1, af[1]);
+#pragma unroll
+                    for (int c = 0; c < QPF; ++c)
+                        if (c < NQC) load_chunk(c, af[c]);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int c = 0; c < NQC; ++c) {
@@ -210,12 +212,12 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
                         for (int i = 0; i < QCH; ++i) {
                             const int kk = c * QCH + i;
                             if (kk < C::KSTEPS) {
-                                S[0] = mfma16x16x32(af[c & 1][2 * i], qB[kk], S[0]);
-                                S[1] = mfma16x16x32(af[c & 1][2 * i + 1], qB[kk], S[1]);
+                                S[0] = mfma16x16x32(af[c % QPF][2 * i], qB[kk], S[0]);
+                                S[1] = mfma16x16x32(af[c % QPF][2 * i + 1], qB[kk], S[1]);
                             }
                         }
                         __builtin_amdgcn_sched_barrier(0);
-                        if (c + 2 < NQC) load_chunk(c + 2, af[c & 1]);
+                        if (c + QPF < NQC) load_chunk(c + QPF, af[c % QPF]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
