@@ -127,6 +127,16 @@ def test_mla_many_sequences(da, oracle_mod, workers):
     compare(out, lse, ref_o, ref_l, "mla b=300 w=%d" % workers)
 
 
+@pytest.mark.parametrize("workers", [0, 3])
+def test_mla_all_sequences_empty(da, workers):
+    """No cache row anywhere (lengths 0 and negative): every row must be out = 0, lse = -inf."""
+    shape = mla_shape(3, 2, 16, 64, 16, 40, seed=33)
+    tensors = wl.make_mla(shape, seqlens=[0, -5, 0])
+    out, lse = run_mla(da, shape, tensors, workers)
+    assert torch.all(out.float() == 0)
+    assert torch.all(torch.isneginf(lse))
+
+
 def test_mla_split_counts_agree(da):
     shape = mla_shape(4, 2, 64, 512, 64, 700, seed=7)
     tensors = wl.make_mla(shape, seqlens=[700, 511, 65, 300])
@@ -266,6 +276,16 @@ def test_gqa_many_sequences(da, oracle_mod, path, workers):
     out, lse = run_gqa(da, shape, tensors, workers, path)
     ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale)
     compare(out, lse, ref_o, ref_l, "gqa b=300 path=%d w=%d" % (path, workers))
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_gqa_all_sequences_empty(da, path):
+    """No cache row anywhere: every row must be out = 0, lse = -inf."""
+    shape = wl.GQAShape(b=2, s=1, hq=8, hkv=2, d=128, t_max=50, scale=0.1, seed=34)
+    tensors = wl.make_gqa(shape, seqlens=[0, -1])
+    out, lse = run_gqa(da, shape, tensors, 0, path)
+    assert torch.all(out.float() == 0)
+    assert torch.all(torch.isneginf(lse))
 
 
 @pytest.mark.parametrize("path", [1, 2])
