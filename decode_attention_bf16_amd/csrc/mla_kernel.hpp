@@ -8,23 +8,27 @@
 // s*h query rows of a sequence are the M dimension of two dense contractions
 // (scores and values) against one shared [tokens, k+p] tile.
 //
-// Work decomposition: a block (4 score waves plus NVW = 8 value waves, three
-// waves per SIMD, when k >= 256; 4 + 4 otherwise) is one worker of the
-// split-KV plan times one block of 64 query rows. The waves have two roles and
-// form a two-stage software pipeline over 32-token tiles:
-//   score waves (0..3), 16 rows each: S^T[32 tokens, 16 rows] = tile . Q^T with
-//     MFMA 16x16x32 bf16 (A = cache tile from LDS, B = the rows' queries held
-//     in registers), then the fp32 online softmax of those rows (exp2 domain,
-//     lazily moved reference maximum). They publish the bf16 probabilities in
-//     the value product's operand layout, the per-row rescale factors when the
-//     reference moved and, at the end of a segment, each row's (max, sum).
+// Work decomposition: a block (4 score waves plus NVW = 4 value waves, two
+// waves per SIMD, when k is a multiple of 128; 4 + 2 otherwise) is one worker
+// of the split-KV plan times one block of 64 query rows. The waves have two
+// roles and form a two-stage software pipeline over 32-token tiles:
+//   score waves (0..3), wave w = 32-row block w/2 x token half w%2 of every
+//     tile: S^T[16 tokens, 32 rows] = tile half . Q^T with MFMA 16x16x32 bf16
+//     (A = 16 cache rows from LDS, read once and used for both 16-row halves;
+//     B = the 32 rows' queries held in registers for the whole segment), then
+//     the fp32 online softmax of those 32 rows over its 16 tokens. Holding 32
+//     rows per wave halves the LDS tile reads against 16-row waves, which is
+//     what bounds a step. The two waves of a row block share one reference
+//     maximum per row (below). They publish the bf16 probabilities in the value
+//     product's operand layout and, at the end of a segment, each row's
+//     (reference, partial sum) of their token half.
 //   value waves (4 .. 3+NVW), all 64 rows x k/NVW latent columns each:
-//     O^T += V^T . P^T with MFMA 32x32x16 bf16 when those columns fill 32-wide
-//     blocks (16x16x32 otherwise), A = latent columns of the same LDS tile
-//     through the transposing LDS read (ds_read_b64_tr_b16), B = the published
-//     probabilities. The first four also copy the cache tiles HBM -> LDS
-//     (buffer_load ... lds, 16 bytes per lane, no registers) two tiles ahead;
-//     all write their columns of the outputs.
+//     O^T += V^T . P^T with MFMA 32x32x16 bf16 (two 16-token k-steps per tile,
+//     one per token half), A = latent columns of the same LDS tile through the
+//     transposing LDS read (ds_read_b64_tr_b16), B = the published
+//     probabilities. They also copy the cache tiles HBM -> LDS (buffer_load ...
+//     lds, 16 bytes per lane, no registers) two tiles ahead, and write their
+//     columns of the outputs.
 // In step j the score waves work on tile j while the value waves work on tile
 // j-1, so on every SIMD one wave's softmax and LDS traffic overlap the other's
 // matrix work, and the score waves never wait for HBM. One barrier per step;
@@ -32,10 +36,19 @@
 // buffer resource covers the sequence's valid rows only, so rows past the
 // sequence length (and padding columns) read as zeros whatever the cache holds.
 //
-// The score MFMA's output layout (lane: query row l%16, tokens 4(l/16)+i and
-// 16+4(l/16)+i) packed to bf16 is directly the value MFMA's B operand when the
-// A operand's tokens are permuted the same way: the transposing reads start at
-// tile rows 4(l/16)+(l%16)/4 and 16 more, which yields exactly those tokens.
+// Shared reference maximum. Probabilities are exp2(score - m) against a lazily
+// moved per-row reference m (moved only when a score exceeds it by more than
+// 2^kRescaleSlack), kept an integer so that every rescale factor is an exact
+// power of two. Both token-half waves of a row start a step with the same m.
+// A wave that must move it uses its own new reference for that step and flags
+// it; after the barrier both waves and the value waves take the larger of the
+// two halves' references as the common one, rescaling the partial row sums,
+// the accumulators and the probabilities of the half that stayed behind (exact
+// in bf16, being a power of two). The common case (no move) costs one flag read.
+//
+// The score MFMA's output layout (lane: query row l%16, tokens 4(l/16)+i of the
+// half) packed to bf16 is directly the value MFMA's B operand for that half's
+// k-step once each lane pair (l/16 = 2c, 2c+1) writes its two 8-byte parts.
 //
 // LDS tile layout: row r (token) holds ROW_CHUNKS 16-byte chunks; logical chunk
 // c is stored at c ^ tile_swz(r) (see tile_swz).
@@ -60,27 +73,24 @@ struct MlaCfg {
     static constexpr int T = kMlaTile;
     static constexpr int TILE_BYTES = T * ROW_BYTES;
     static constexpr int NBUF = 4;
-    // value waves: eight when k >= 256 (each owns k/8 latent columns), else four
-    static constexpr int NVW = K >= 256 ? 8 : 4;
+    // value waves: four when k is a multiple of 128 (each owns k/4 latent
+    // columns), else two (k/2 columns, a multiple of 32)
+    static constexpr int NVW = K % 128 == 0 ? 4 : 2;
     static constexpr int THREADS = 64 * (4 + NVW);
     static constexpr int ROWS = kMlaRows;
-    static constexpr int LPW = T * ROW_CHUNKS / 256;            // copy instructions per value wave per tile
-    static_assert(T * ROW_CHUNKS % 256 == 0, "tile chunks divisible among the four copying waves");
-    static constexpr int CBV = K / (16 * NVW);                  // 16-column output blocks per value wave
-    // value product with v_mfma_f32_32x32x16_bf16 (two chained 16-token k-steps
-    // per accumulator and tile) when a value wave's columns fill 32-column blocks
-    static constexpr bool WIDE = K % (32 * NVW) == 0;
+    static constexpr int LPW = T * ROW_CHUNKS / (64 * NVW);     // copy instructions per value wave per tile
+    static_assert(T * ROW_CHUNKS % (64 * NVW) == 0, "tile chunks divisible among the value waves");
     static constexpr int CB32 = K / (32 * NVW);                 // 32-column output blocks per value wave
     static constexpr int QCH = 2;                               // score k-steps per LDS read chunk
     static constexpr int QPF = 2;                               // chunks in flight ahead of the MFMAs
-    static constexpr int PBUF_OFF = NBUF * TILE_BYTES;          // [2 slots][4 row blocks][64 lanes] x 16 B
-    static constexpr int ALPHA_OFF = PBUF_OFF + 2 * 4 * 64 * 16;  // [2 slots][64 rows] float
-    static constexpr int FLAG_OFF = ALPHA_OFF + 2 * 64 * 4;       // [2 slots][4 row blocks] int
-    static constexpr int SEG_OFF = FLAG_OFF + 2 * 4 * 4;          // [2 slots][64 rows] (max, sum)
-    static constexpr int LDS_BYTES = SEG_OFF + 2 * 64 * 8;
+    static constexpr int PBUF_OFF = NBUF * TILE_BYTES;          // [2 slots][2 row blocks][2 halves][64 lanes] x 16 B
+    static constexpr int MREF_OFF = PBUF_OFF + 2 * 4 * 64 * 16;   // [2 slots][2 halves][64 rows] float
+    static constexpr int FLAG_OFF = MREF_OFF + 2 * 2 * 64 * 4;    // [2 slots][4 score waves] int
+    static constexpr int SEG_OFF = FLAG_OFF + 2 * 4 * 4;          // [2 slots][2 halves][64 rows] (ref, sum)
+    static constexpr int LDS_BYTES = SEG_OFF + 2 * 2 * 64 * 8;
     static_assert(LDS_BYTES <= 163840, "LDS budget");
     // LDS read offsets that the compiler folds into the 16-bit instruction offset
-    static_assert(16 * ROW_BYTES + 128 * ((KSTEPS - 1) / 2) + 128 < 65536, "score read offsets");
+    static_assert(128 * ((KSTEPS - 1) / 2) + 128 < 65536, "score read offsets");
     static_assert(16 * ROW_BYTES + 2 * K + 128 < 65536, "value read offsets");
 };
 
@@ -97,6 +107,17 @@ __device__ __forceinline__ int tile_swz(int r)
 {
     const int i0 = (r >> 1) & 1, i1 = (r >> 2) & 1, i2 = (r >> 3) & 1;
     return (i0 ^ i2) | (i0 << 1) | ((i1 ^ i2) << 2);
+}
+
+// Eight bf16 values times a power of two (exact unless the result leaves the
+// normal range; rounded to nearest even then).
+__device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8 &v, float f)
+{
+    const u32x4 u = __builtin_bit_cast(u32x4, v);
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(bf16lo_to_f32(u[i]) * f, bf16hi_to_f32(u[i]) * f);
+    return __builtin_bit_cast(bf16x8, r);
 }
 
 template <int K, int P>
@@ -133,73 +154,92 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
     const int M = s * h;  // query rows per sequence
 
     DA_LDS char *pbuf = lds + C::PBUF_OFF;
-    DA_LDS float *alpha_buf = (DA_LDS float *)(lds + C::ALPHA_OFF);
+    DA_LDS float *mref_buf = (DA_LDS float *)(lds + C::MREF_OFF);
     DA_LDS int *flag_buf = (DA_LDS int *)(lds + C::FLAG_OFF);
     DA_LDS float *seg_buf = (DA_LDS float *)(lds + C::SEG_OFF);
 
     if (w < 4) {
         // ============================================================ score waves
-        const int sw = w;
-        const int row = rb * C::ROWS + sw * 16 + n;  // this lane's query row
-        const bool row_ok = row < M;
-        const int sq = tile_swz(n);  // rows n and n + 16 share it
-        const int qk_off0 = n * C::ROW_BYTES + ((g ^ sq) << 4);        // even k-steps
-        const int qk_off1 = n * C::ROW_BYTES + (((4 + g) ^ sq) << 4);  // odd k-steps
+        const int r2 = w >> 1;          // 32-row block of the block's 64 rows
+        const int tb = w & 1;           // token half: tokens 16 tb .. 16 tb + 15 of every tile
+        const int rowl = 32 * r2 + n;   // block-local rows rowl (rr = 0) and rowl + 16 (rr = 1)
+        int row[2];
+        bool row_ok[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            row[rr] = rb * C::ROWS + rowl + 16 * rr;
+            row_ok[rr] = row[rr] < M;
+        }
+        const int sq = tile_swz(n);  // = tile_swz(16 tb + n): the swizzle ignores bit 4
+        const int trow = (16 * tb + n) * C::ROW_BYTES;
+        const int qk_off0 = trow + ((g ^ sq) << 4);        // even k-steps
+        const int qk_off1 = trow + (((4 + g) ^ sq) << 4);  // odd k-steps
 
-        bf16x8 qB[C::KSTEPS];
-        float mref = -INFINITY, lsum = 0.f;
-        int nvis = 0, nvis_min = 0;
+        bf16x8 qB[2][C::KSTEPS];
+        // mref: the common reference of the rows at the start of a step (log2
+        // units, integer or -inf); muse: this wave's reference in the step just
+        // done; moved: whether this wave moved it there
+        float mref[2] = {-INFINITY, -INFINITY}, muse[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+        bool moved = false;
+        int nvis[2] = {0, 0}, nvis_min = 0;
         PlanWalk cur = plan;
+        // a segment starts: its rows' queries, visible lengths and fresh softmax state
+        auto start_segment = [&]() {
+            const int L = clamp_len(seqlens[cur.b], t_max);
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                nvis[rr] = row_ok[rr] ? (L - s + row[rr] / h + 1) : 0;
+#pragma unroll
+                for (int kk = 0; kk < C::KSTEPS; ++kk) {
+                    u32x4 v = {0u, 0u, 0u, 0u};
+                    const int e0 = kk * 32 + g * 8;
+                    if (row_ok[rr]) {
+                        if (e0 < K)
+                            v = *(const u32x4 *)(q_lat + ((size_t)cur.b * M + row[rr]) * K + e0);
+                        else if (e0 - K < P)
+                            v = *(const u32x4 *)(q_rope + ((size_t)cur.b * M + row[rr]) * P + (e0 - K));
+                    }
+                    qB[rr][kk] = as_bf16x8(v);
+                }
+                mref[rr] = -INFINITY;
+                muse[rr] = -INFINITY;
+                lsum[rr] = 0.f;
+            }
+            moved = false;
+            int mn = min(nvis[0], nvis[1]);
+            for (int off = 1; off < 64; off <<= 1) mn = min(mn, __shfl_xor(mn, off));
+            nvis_min = mn;
+        };
+        start_segment();  // the first queries load while the first tiles are copied
 
         lds_barrier();  // tile 0 has landed
         for (int j = 0; j <= ntiles; ++j) {
             if (j < ntiles) {
                 const int tt = tile_lo + j;
-                const bool new_seg = j == 0 || tt >= cur.te;
+                const bool new_seg = j > 0 && tt >= cur.te;
                 cur.seek(seqlens, tt);
-                if (new_seg) {
-                    const int L = clamp_len(seqlens[cur.b], t_max);
-                    nvis = row_ok ? (L - s + row / h + 1) : 0;
-#pragma unroll
-                    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-                        u32x4 v = {0u, 0u, 0u, 0u};
-                        const int e0 = kk * 32 + g * 8;
-                        if (row_ok) {
-                            if (e0 < K)
-                                v = *(const u32x4 *)(q_lat + ((size_t)cur.b * M + row) * K + e0);
-                            else if (e0 - K < P)
-                                v = *(const u32x4 *)(q_rope + ((size_t)cur.b * M + row) * P + (e0 - K));
-                        }
-                        qB[kk] = as_bf16x8(v);
-                    }
-                    mref = -INFINITY;
-                    lsum = 0.f;
-                    int mn = nvis;
-                    for (int off = 1; off < 64; off <<= 1) mn = min(mn, __shfl_xor(mn, off));
-                    nvis_min = mn;
-                }
+                const int slot = j & 1;
+                // the partner half's flag of the previous step, consumed after the MFMAs
+                int pflag = 0;
+                if (j > 0 && !new_seg) pflag = flag_buf[(slot ^ 1) * 4 + (w ^ 1)];
+                if (new_seg) start_segment();
                 const DA_LDS char *tile = lds + (j % C::NBUF) * C::TILE_BYTES;
 
-                // S^T[32 tokens, 16 rows]. The tile's A fragments are read in
+                // S^T[16 tokens, 32 rows]. The tile's A fragments are read in
                 // chunks of QCH k-steps, QPF chunks ahead of the MFMAs that use
-                // them, so LDS latency hides behind matrix work. Each 16-token
-                // block accumulates in one chain: back-to-back MFMAs on the same
-                // accumulator forward it without a register read, which measured
-                // faster than spreading the k-steps over more accumulators.
+                // them, so LDS latency hides behind matrix work; each fragment
+                // feeds the MFMAs of both 16-row halves.
                 f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
                 {
                     constexpr int QCH = C::QCH, QPF = C::QPF;
                     constexpr int NQC = (C::KSTEPS + QCH - 1) / QCH;
-                    bf16x8 af[QPF][2 * QCH];
-                    auto load_chunk = [&](int c, bf16x8(&d)[2 * QCH]) {
+                    bf16x8 af[QPF][QCH];
+                    auto load_chunk = [&](int c, bf16x8(&d)[QCH]) {
 #pragma unroll
                         for (int i = 0; i < QCH; ++i) {
                             const int kk = c * QCH + i;
-                            if (kk < C::KSTEPS) {
-                                const DA_LDS char *p = tile + ((kk & 1) ? qk_off1 : qk_off0) + 128 * (kk >> 1);
-                                d[2 * i] = *(const DA_LDS bf16x8 *)(p);
-                                d[2 * i + 1] = *(const DA_LDS bf16x8 *)(p + 16 * C::ROW_BYTES);
-                            }
+                            if (kk < C::KSTEPS)
+                                d[i] = *(const DA_LDS bf16x8 *)(tile + ((kk & 1) ? qk_off1 : qk_off0) + 128 * (kk >> 1));
                         }
                     };
 #pragma unroll
@@ -212,8 +252,8 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
                         for (int i = 0; i < QCH; ++i) {
                             const int kk = c * QCH + i;
                             if (kk < C::KSTEPS) {
-                                S[0] = mfma16x16x32(af[c % QPF][2 * i], qB[kk], S[0]);
-                                S[1] = mfma16x16x32(af[c % QPF][2 * i + 1], qB[kk], S[1]);
+                                S[0] = mfma16x16x32(af[c % QPF][i], qB[0][kk], S[0]);
+                                S[1] = mfma16x16x32(af[c % QPF][i], qB[1][kk], S[1]);
                             }
                         }
                         __builtin_amdgcn_sched_barrier(0);
@@ -222,65 +262,76 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
                     }
                 }
                 // draft / length mask, only on tiles that reach past some row's visible end
-                const int tok0 = (tt - cur.ts) * C::T;
-                if (tok0 + C::T > nvis_min) {
+                const int tokh = (tt - cur.ts) * C::T + 16 * tb;  // first token of this half
+                if (tokh + 16 > nvis_min) {
 #pragma unroll
-                    for (int bt = 0; bt < 2; ++bt)
+                    for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            if (tok0 + bt * 16 + g * 4 + i >= nvis) S[bt][i] = -INFINITY;
+                            if (tokh + 4 * g + i >= nvis[rr]) S[rr][i] = -INFINITY;
                 }
-                // online softmax of the 16 rows. Lane (n, g) holds 8 scores of
-                // row n; the row's reference maximum mref is kept identical on
-                // the row's four lanes (g = 0..3). A lane-local test decides
-                // whether any reference must move (rare: mostly the first tile
-                // of a segment); only then is the row maximum formed across the
-                // four lanes. Row sums stay per lane until the segment ends.
-                float m = -INFINITY;
+                // the common reference after the previous step: the larger of the
+                // two halves' references (both waves of the row block agree)
+                const bool pf = __builtin_amdgcn_readfirstlane(pflag) != 0;
+                if (pf || moved) {
 #pragma unroll
-                for (int bt = 0; bt < 2; ++bt)
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const float mp = pf ? mref_buf[((slot ^ 1) * 2 + (tb ^ 1)) * 64 + rowl + 16 * rr] : mref[rr];
+                        const float mc = fmaxf(muse[rr], mp);
+                        lsum[rr] *= mc == -INFINITY ? 1.f : fast_exp2(muse[rr] - mc);
+                        mref[rr] = mc;
+                    }
+                }
+                // online softmax of the 32 rows over this half's 16 tokens. Lane
+                // (n, g) holds 4 scores of each of rows rowl and rowl + 16; the
+                // references are kept identical on a row's four lanes (g = 0..3).
+                // A lane-local test decides whether any reference must move
+                // (rare: mostly the first tile of a segment); only then is the
+                // row maximum formed across the four lanes.
+                float m[2] = {-INFINITY, -INFINITY};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) m = fmaxf(m, S[bt][i]);
-                const int slot = j & 1;
-                const bool upd = __builtin_amdgcn_ballot_w64(m * scale_log2 > mref + kRescaleSlack) != 0;
+                for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m[rr] = fmaxf(m[rr], S[rr][i]);
+                const bool upd = __builtin_amdgcn_ballot_w64(m[0] * scale_log2 > mref[0] + kRescaleSlack ||
+                                                             m[1] * scale_log2 > mref[1] + kRescaleSlack) != 0;
+                float mu[2] = {mref[0], mref[1]};
                 if (upd) {
-                    const float mt = wave_max_across_groups16(m) * scale_log2;  // row max, log2 units
-                    const float mnew = fmaxf(mref, mt);
-                    const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref - mnew);
-                    mref = mnew;
-                    lsum *= alpha;
-                    if (g == 0) alpha_buf[slot * 64 + sw * 16 + n] = alpha;
-                }
-                if (lane == 0) flag_buf[slot * 4 + sw] = upd ? 1 : 0;
-                const float ms = mref == -INFINITY ? 0.f : mref;
-                uint32_t pk[4];
 #pragma unroll
-                for (int bt = 0; bt < 2; ++bt) {
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const float mt = wave_max_across_groups16(m[rr]) * scale_log2;  // row max, log2 units
+                        mu[rr] = fmaxf(mref[rr], __builtin_ceilf(mt));
+                        lsum[rr] *= mu[rr] == -INFINITY ? 1.f : fast_exp2(mref[rr] - mu[rr]);
+                        if (g == 0) mref_buf[(slot * 2 + tb) * 64 + rowl + 16 * rr] = mu[rr];
+                    }
+                }
+                if (lane == 0) flag_buf[slot * 4 + w] = upd ? 1 : 0;
+                moved = upd;
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    muse[rr] = mu[rr];
+                    const float ms = mu[rr] == -INFINITY ? 0.f : mu[rr];
                     float p[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        p[i] = fast_exp2(__builtin_fmaf(S[bt][i], scale_log2, -ms));
-                        lsum += p[i];
+                        p[i] = fast_exp2(__builtin_fmaf(S[rr][i], scale_log2, -ms));
+                        lsum[rr] += p[i];
                     }
-                    pk[2 * bt] = pack_bf16x2(p[0], p[1]);
-                    pk[2 * bt + 1] = pack_bf16x2(p[2], p[3]);
-                }
-                if constexpr (C::WIDE) {
-                    // B operand of the 32x32x16 value MFMA: [row block of 32][k-step][lane]
-                    // 16 bytes, lane l = row l%32 and tokens 16*ks + 8*(l/32) + 0..7
-                    const int l2 = 32 * (g >> 1) + 16 * (sw & 1) + n;
-#pragma unroll
-                    for (int bt = 0; bt < 2; ++bt)
-                        *(DA_LDS u32x2 *)(pbuf + ((((slot * 2 + (sw >> 1)) * 2 + bt) * 64 + l2) * 16 + 8 * (g & 1))) =
-                            u32x2{pk[2 * bt], pk[2 * bt + 1]};
-                } else {
-                    *(DA_LDS u32x4 *)(pbuf + ((slot * 4 + sw) * 64 + lane) * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+                    // B operand of the 32x32x16 value MFMA: [slot][row block][half][lane]
+                    // 16 bytes, lane l = row l%32 of the block and tokens 8(l/32) + 0..7
+                    // of the half; this lane holds tokens 4g .. 4g + 3 of the half
+                    const int l2 = 32 * (g >> 1) + 16 * rr + n;
+                    *(DA_LDS u32x2 *)(pbuf + ((((slot * 2 + r2) * 2 + tb) * 64 + l2) * 16 + 8 * (g & 1))) =
+                        u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
                 }
                 if (tt + 1 >= cur.te || j + 1 == ntiles) {
-                    const float ls = wave_sum_across_groups16(lsum);
-                    if (g == 0) {
-                        seg_buf[(slot * 64 + sw * 16 + n) * 2 + 0] = mref;
-                        seg_buf[(slot * 64 + sw * 16 + n) * 2 + 1] = ls;
+#pragma unroll
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const float ls = wave_sum_across_groups16(lsum[rr]);
+                        if (g == 0) {
+                            seg_buf[((slot * 2 + tb) * 64 + rowl + 16 * rr) * 2 + 0] = mu[rr];
+                            seg_buf[((slot * 2 + tb) * 64 + rowl + 16 * rr) * 2 + 1] = ls;
+                        }
                     }
                 }
             }
@@ -289,22 +340,6 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
     } else {
         // ============================================================ value waves
         const int vw = w - 4;
-        const int trr = 4 * g + (n >> 2);  // first tile row of this lane's transposing read
-        const int st = tile_swz(trr);      // rows trr and trr + 16 share it
-        const int hsel = (n & 3) >> 1;
-        const int tr_row = trr * C::ROW_BYTES + ((n & 1) << 3);
-        int tr_off[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) tr_off[jj] = tr_row + (((2 * jj + hsel) ^ st) << 4);
-        // byte offset (within a tile) of this lane's read for output column block cb
-        auto tr_addr = [&](int cb) -> int {
-            if constexpr (C::CBV % 4 == 0) {
-                return tr_off[cb & 3] + 128 * (vw * (C::CBV / 4) + (cb >> 2));
-            } else {
-                const int jj = vw * C::CBV + cb;  // 16-column block across the full latent width
-                return tr_row + (((2 * (jj & 3) + hsel) ^ st) << 4) + 128 * (jj >> 2);
-            }
-        };
 
         // HBM -> LDS copy of tile j of this worker into buffer j % NBUF:
         // copy_setup resolves the sequence, copy_part issues copy instruction
@@ -323,12 +358,12 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
             tile_bytes_in_seq = (uint32_t)(tt - dma.ts) * C::T * C::KP * 2;
         };
         auto copy_part = [&](int j, const u32x4 &rsrc, uint32_t tile_bytes_in_seq, int it) {
-            const int pch = (it * 4 + vw) * 64 + lane;  // physical chunk within the tile
+            const int pch = (it * C::NVW + vw) * 64 + lane;  // physical chunk within the tile
             const int r = pch / C::ROW_CHUNKS;
             const int c = (pch - r * C::ROW_CHUNKS) ^ tile_swz(r);
             const uint32_t off =
                 c < C::SRC_CHUNKS ? (uint32_t)((r * C::KP + c * 8) * 2) + tile_bytes_in_seq : 0x80000000u;
-            lds_dma16(rsrc, lds + (j % C::NBUF) * C::TILE_BYTES + (it * 4 + vw) * 1024, off);
+            lds_dma16(rsrc, lds + (j % C::NBUF) * C::TILE_BYTES + (it * C::NVW + vw) * 1024, off);
         };
         auto issue_tile = [&](int j) {
             u32x4 rsrc;
@@ -338,53 +373,45 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
             for (int it = 0; it < C::LPW; ++it) copy_part(j, rsrc, tbs, it);
         };
 
-        // accumulators: narrow form [16-row block][16-column block] (16x16x32),
-        // wide form [32-row block][32-column block] (32x32x16)
+        // accumulators [32-row block][32-column block]; lane l holds query row
+        // 32 r2 + l%32 of the block. macc: the reference of those rows.
         typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-        constexpr int NA4 = C::WIDE ? 1 : 4, NAC = C::WIDE ? 1 : C::CBV;
-        constexpr int NW2 = C::WIDE ? 2 : 1, NWC = C::WIDE ? C::CB32 : 1;
-        f32x4 acc[NA4][NAC];
-        f32x16 acw[NW2][NWC];
+        f32x16 acw[2][C::CB32];
+        float macc[2] = {-INFINITY, -INFINITY};
         auto zero_acc = [&]() {
-            if constexpr (C::WIDE) {
 #pragma unroll
-                for (int r = 0; r < NW2; ++r)
+            for (int r = 0; r < 2; ++r) {
+                macc[r] = -INFINITY;
 #pragma unroll
-                    for (int cb = 0; cb < NWC; ++cb)
+                for (int cb = 0; cb < C::CB32; ++cb)
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) acw[r][cb][e] = 0.f;
-            } else {
-#pragma unroll
-                for (int r4 = 0; r4 < NA4; ++r4)
-#pragma unroll
-                    for (int cb = 0; cb < NAC; ++cb) acc[r4][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int e = 0; e < 16; ++e) acw[r][cb][e] = 0.f;
             }
         };
         zero_acc();
-        // wide form: byte offset (within a tile) of transposing read h of k-step
-        // ks for 32-column block cb; lane l gets tokens 16ks + 8(l/32) + 4h + 0..3
-        // of column 32cb + l%32 of this wave's columns
-        auto tr32_addr = [&](int cb, int ks, int h) -> int {
-            const int tok = 16 * ks + 8 * (g >> 1) + 4 * h + (n >> 2);
+        // byte offset (within a tile) of transposing read hh of k-step ks for
+        // 32-column block cb; lane l gets tokens 16ks + 8(l/32) + 4hh + 0..3 of
+        // column 32cb + l%32 of this wave's columns
+        auto tr32_addr = [&](int cb, int ks, int hh) -> int {
+            const int tok = 16 * ks + 8 * (g >> 1) + 4 * hh + (n >> 2);
             const int chunk = (vw * (K / C::NVW) + 32 * cb) / 8 + 2 * (g & 1) + ((n >> 1) & 1);
             return tok * C::ROW_BYTES + (((chunk & ~7) | ((chunk ^ tile_swz(tok)) & 7)) << 4) + ((n & 1) << 3);
         };
         PlanWalk cur = plan;
 
-        // the first four value waves copy the tiles (LPW copies each per tile)
-        const bool copier = vw < 4;
-        if (copier) {
-            issue_tile(0);
-            if (ntiles > 1) {
-                issue_tile(1);
-                wait_vmcnt<C::LPW>();
-            } else {
-                wait_vmcnt<0>();
-            }
-        }
+        // the first three tiles before step 0 (buffers 0..2), then tile j+2 in step j >= 1
+        issue_tile(0);
+        if (ntiles > 1) issue_tile(1);
+        if (ntiles > 2) issue_tile(2);
+        if (ntiles > 2)
+            wait_vmcnt<2 * C::LPW>();
+        else if (ntiles > 1)
+            wait_vmcnt<C::LPW>();
+        else
+            wait_vmcnt<0>();
         lds_barrier();  // tile 0 has landed
         for (int j = 0; j <= ntiles; ++j) {
-            const bool issued = copier && j + 2 < ntiles;
+            const bool issued = j >= 1 && j + 2 < ntiles;
             bool stored = false;
             const int tt = tile_lo + j - 1;
             const int slot = (j - 1) & 1;
@@ -393,29 +420,19 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
             // transposed latent fragment), the copy and the matrix work after them
             u32x4 fl = {0u, 0u, 0u, 0u};
             bf16x8 pB[4];
-            constexpr int NTR = C::WIDE ? 4 * C::CB32 : C::CBV;
-            i16x4 vlo[NTR], vhi[NTR];
+            i16x4 vlo[2 * C::CB32], vhi[2 * C::CB32];
             if (j >= 1) {
                 fl = *(const DA_LDS u32x4 *)(flag_buf + slot * 4);
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4)
                     pB[r4] = *(const DA_LDS bf16x8 *)(pbuf + ((slot * 4 + r4) * 64 + lane) * 16);
-                if constexpr (C::WIDE) {
 #pragma unroll
-                    for (int cb = 0; cb < C::CB32; ++cb)
+                for (int cb = 0; cb < C::CB32; ++cb)
 #pragma unroll
-                        for (int ks = 0; ks < 2; ++ks) {
-                            vlo[2 * cb + ks] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(tile + tr32_addr(cb, ks, 0)));
-                            vhi[2 * cb + ks] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(tile + tr32_addr(cb, ks, 1)));
-                        }
-                } else {
-#pragma unroll
-                    for (int cb = 0; cb < C::CBV; ++cb) {
-                        const DA_LDS char *vb = tile + tr_addr(cb);
-                        vlo[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(vb));
-                        vhi[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(vb + 16 * C::ROW_BYTES));
+                    for (int ks = 0; ks < 2; ++ks) {
+                        vlo[2 * cb + ks] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(tile + tr32_addr(cb, ks, 0)));
+                        vhi[2 * cb + ks] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(tile + tr32_addr(cb, ks, 1)));
                     }
-                }
             }
             __builtin_amdgcn_sched_barrier(0);
             // the copy of tile j+2 is spread over the matrix work below, so that
@@ -423,83 +440,57 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
             u32x4 crsrc = {0u, 0u, 0u, 0u};
             uint32_t ctbs = 0;
             if (issued) copy_setup(j + 2, crsrc, ctbs);
-            if (j == 0 && issued) {
-#pragma unroll
-                for (int it = 0; it < C::LPW; ++it) copy_part(j + 2, crsrc, ctbs, it);
-            }
             __builtin_amdgcn_sched_barrier(0);
             if (j >= 1) {
                 const bool new_seg = j == 1 || tt >= cur.te;
                 cur.seek(seqlens, tt);
                 if (new_seg) zero_acc();
-                // rows whose reference maximum moved: bring the sums to the new reference
+                // a half moved its reference: take the larger of the two as the
+                // rows' reference and bring the sums and the other half's
+                // probabilities to it (powers of two)
                 if (__builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3])) {
-                    if constexpr (C::WIDE) {
 #pragma unroll
-                        for (int r2 = 0; r2 < 2; ++r2) {
-                            const int r4 = 2 * r2 + (g & 1);  // this lane's 16-row block
-                            const float al = fl[r4] ? alpha_buf[slot * 64 + 16 * r4 + n] : 1.f;
+                    for (int r2 = 0; r2 < 2; ++r2) {
+                        if (__builtin_amdgcn_readfirstlane(fl[2 * r2] | fl[2 * r2 + 1])) {
+                            const int rl = 32 * r2 + (lane & 31);
+                            const float ma = fl[2 * r2] ? mref_buf[(slot * 2 + 0) * 64 + rl] : macc[r2];
+                            const float mb = fl[2 * r2 + 1] ? mref_buf[(slot * 2 + 1) * 64 + rl] : macc[r2];
+                            const float mc = fmaxf(ma, mb);
+                            if (mc != -INFINITY) {
+                                const float al = fast_exp2(macc[r2] - mc);
 #pragma unroll
-                            for (int cb = 0; cb < C::CB32; ++cb) acw[r2][cb] *= al;
-                        }
-                    } else {
-#pragma unroll
-                        for (int r4 = 0; r4 < NA4; ++r4) {
-                            if (__builtin_amdgcn_readfirstlane(fl[r4])) {
-                                const float al = alpha_buf[slot * 64 + r4 * 16 + n];
-#pragma unroll
-                                for (int cb = 0; cb < NAC; ++cb) acc[r4][cb] *= al;
+                                for (int cb = 0; cb < C::CB32; ++cb) acw[r2][cb] *= al;
+                                pB[2 * r2] = scale_bf16x8(pB[2 * r2], fast_exp2(ma - mc));
+                                pB[2 * r2 + 1] = scale_bf16x8(pB[2 * r2 + 1], fast_exp2(mb - mc));
                             }
+                            macc[r2] = mc;
                         }
                     }
                 }
-                if constexpr (C::WIDE) {
-                    // pB[2 * r2 + ks] = B operand of 32-row block r2, k-step ks
+                // pB[2 * r2 + ks] = B operand of 32-row block r2, k-step (token half) ks
 #pragma unroll
-                    for (int cb = 0; cb < C::CB32; ++cb) {
-                        const bf16x8 a0 = __builtin_bit_cast(
-                            bf16x8, __builtin_shufflevector(vlo[2 * cb], vhi[2 * cb], 0, 1, 2, 3, 4, 5, 6, 7));
-                        const bf16x8 a1 = __builtin_bit_cast(
-                            bf16x8, __builtin_shufflevector(vlo[2 * cb + 1], vhi[2 * cb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+                for (int cb = 0; cb < C::CB32; ++cb) {
+                    const bf16x8 a0 = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(vlo[2 * cb], vhi[2 * cb], 0, 1, 2, 3, 4, 5, 6, 7));
+                    const bf16x8 a1 = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(vlo[2 * cb + 1], vhi[2 * cb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-                        for (int r2 = 0; r2 < 2; ++r2) {
-                            acw[r2][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, pB[2 * r2], acw[r2][cb], 0, 0, 0);
-                            acw[r2][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pB[2 * r2 + 1], acw[r2][cb], 0, 0, 0);
-                        }
-                        if (issued) {
-#pragma unroll
-                            for (int it = 0; it < C::LPW; ++it)
-                                if ((it * C::CB32) / C::LPW == cb) copy_part(j + 2, crsrc, ctbs, it);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
+                    for (int r2 = 0; r2 < 2; ++r2) {
+                        acw[r2][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, pB[2 * r2], acw[r2][cb], 0, 0, 0);
+                        acw[r2][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pB[2 * r2 + 1], acw[r2][cb], 0, 0, 0);
                     }
-                } else {
+                    if (issued) {
 #pragma unroll
-                    for (int cb = 0; cb < C::CBV; ++cb) {
-                        const bf16x8 a = __builtin_bit_cast(
-                            bf16x8, __builtin_shufflevector(vlo[cb], vhi[cb], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) acc[r4][cb] = mfma16x16x32(a, pB[r4], acc[r4][cb]);
-                        if (issued) {
-#pragma unroll
-                            for (int it = 0; it < C::LPW; ++it)
-                                if ((it * C::CBV) / C::LPW == cb) copy_part(j + 2, crsrc, ctbs, it);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
+                        for (int it = 0; it < C::LPW; ++it)
+                            if ((it * C::CB32) / C::LPW == cb) copy_part(j + 2, crsrc, ctbs, it);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 // end of a segment: normalize and write the result or the partial
                 if (tt + 1 >= cur.te || j == ntiles) {
                     const int bq = cur.b;
                     const int nseg = cur.ns;
                     const int sl = cur.slot(worker);
-                    // normalization of query row rloc (row of the block) and its output place
-                    auto row_info = [&](int rloc, float &inv, float &lse2) {
-                        const float mr = seg_buf[(slot * 64 + rloc) * 2 + 0];
-                        const float ls = seg_buf[(slot * 64 + rloc) * 2 + 1];
-                        inv = ls > 0.f ? 1.f / ls : 0.f;
-                        lse2 = ls > 0.f ? mr + fast_log2(ls) : -INFINITY;
-                    };
                     auto put4 = [&](int row, int col, const f32x4 &v, float inv) {
                         if (nseg == 1) {
                             *(u32x2 *)(out + ((size_t)bq * M + row) * K + col) =
@@ -508,49 +499,39 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
                             *(f32x4 *)(part_out + ((size_t)sl * M + row) * K + col) = v * inv;
                         }
                     };
-                    auto put_lse = [&](int row, float lse2) {
-                        // one writer per row: the wide layout spreads a row block over
-                        // lane groups 0 and 1, the narrow one keeps it in group 0
-                        if ((C::WIDE ? (g >> 1) : g) != 0 || vw != 0) return;
-                        if (nseg == 1)
-                            lse[(size_t)bq * M + row] = lse2 * kLn2;
-                        else
-                            part_lse[(size_t)sl * M + row] = lse2;
-                    };
-                    if constexpr (C::WIDE) {
 #pragma unroll
-                        for (int r2 = 0; r2 < 2; ++r2) {
-                            // lane l: query row 32*r2 + l%32; value e of block cb is column
-                            // 32cb + 8(e/4) + 4(l/32) + e%4 of this wave's columns
-                            const int rloc = 32 * r2 + 16 * (g & 1) + n;
-                            const int row = rb * C::ROWS + rloc;
-                            if (row < M) {
-                                float inv, lse2;
-                                row_info(rloc, inv, lse2);
-                                const int col0 = vw * (K / C::NVW) + 4 * (g >> 1);
+                    for (int r2 = 0; r2 < 2; ++r2) {
+                        // lane l: query row 32*r2 + l%32; value e of block cb is column
+                        // 32cb + 8(e/4) + 4(l/32) + e%4 of this wave's columns
+                        const int rloc = 32 * r2 + (lane & 31);
+                        const int row = rb * C::ROWS + rloc;
+                        if (row < M) {
+                            // the row's sum over both halves, at the common reference
+                            const float mc = macc[r2];
+                            float l = 0.f;
 #pragma unroll
-                                for (int cb = 0; cb < C::CB32; ++cb)
-#pragma unroll
-                                    for (int qq = 0; qq < 4; ++qq)
-                                        put4(row, col0 + 32 * cb + 8 * qq,
-                                             f32x4{acw[r2][cb][4 * qq], acw[r2][cb][4 * qq + 1], acw[r2][cb][4 * qq + 2],
-                                                   acw[r2][cb][4 * qq + 3]},
-                                             inv);
-                                put_lse(row, lse2);
+                            for (int hh = 0; hh < 2; ++hh) {
+                                const float mh = seg_buf[((slot * 2 + hh) * 64 + rloc) * 2 + 0];
+                                const float lh = seg_buf[((slot * 2 + hh) * 64 + rloc) * 2 + 1];
+                                if (lh > 0.f) l += lh * fast_exp2(mh - mc);
                             }
-                        }
-                    } else {
+                            const float inv = l > 0.f ? 1.f / l : 0.f;
+                            const float lse2 = l > 0.f ? mc + fast_log2(l) : -INFINITY;
+                            const int col0 = vw * (K / C::NVW) + 4 * (g >> 1);
 #pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) {
-                            const int rloc = 16 * r4 + n;
-                            const int row = rb * C::ROWS + rloc;
-                            if (row < M) {
-                                float inv, lse2;
-                                row_info(rloc, inv, lse2);
-                                const int col0 = vw * (K / C::NVW) + g * 4;
+                            for (int cb = 0; cb < C::CB32; ++cb)
 #pragma unroll
-                                for (int cb = 0; cb < C::CBV; ++cb) put4(row, col0 + 16 * cb, acc[r4][cb], inv);
-                                put_lse(row, lse2);
+                                for (int qq = 0; qq < 4; ++qq)
+                                    put4(row, col0 + 32 * cb + 8 * qq,
+                                         f32x4{acw[r2][cb][4 * qq], acw[r2][cb][4 * qq + 1], acw[r2][cb][4 * qq + 2],
+                                               acw[r2][cb][4 * qq + 3]},
+                                         inv);
+                            // one writer per row: lanes 0..31 of the first value wave
+                            if (g < 2 && vw == 0) {
+                                if (nseg == 1)
+                                    lse[(size_t)bq * M + row] = lse2 * kLn2;
+                                else
+                                    part_lse[(size_t)sl * M + row] = lse2;
                             }
                         }
                     }
@@ -558,8 +539,10 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
                 }
             }
             // tile j+1 (issued a step ago) must be in LDS before the barrier publishes it
-            if (copier && j + 1 < ntiles) {
-                if (issued && !stored)
+            // (tile j+2, if any, was issued after it: in this step, or before step 0
+            // when j = 0; the epilogue's stores come after both)
+            if (j + 1 < ntiles) {
+                if (j + 2 < ntiles && !stored)
                     wait_vmcnt<C::LPW>();
                 else
                     wait_vmcnt<0>();
