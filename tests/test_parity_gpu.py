@@ -194,6 +194,28 @@ def test_mla_huge_late_score(da, oracle_mod, workers, late_row, mag):
     compare(out, lse, ref_o, ref_l, "huge late score row %d workers %d" % (late_row, workers))
 
 
+@pytest.mark.parametrize("workers", [1, 2])
+@pytest.mark.parametrize("pos", [(40, 57, 6.0, 4.0), (40, 57, 4.0, 6.0), (70, 90, 24.0, 12.0), (33, 34, 5.0, 5.0)])
+def test_mla_score_jumps_in_both_token_halves(da, oracle_mod, workers, pos):
+    """Two cache rows of one 32-token tile, one in each 16-token half, whose
+    scores jump far above everything before them by different amounts (or the
+    same, or in two adjacent tiles): each half's softmax reference moves in the
+    same step, and the common reference must be the larger of the two
+    (also: both rows in one half, and jumps in different tiles)."""
+    r0, r1, m0, m1 = pos
+    shape = mla_shape(2, 1, 64, 512, 64, 200, seed=13)
+    ql, qr, c, sl = wl.make_mla(shape, seqlens=[200, 160])
+    for bq, rows_mags in enumerate([((r0, m0), (r1, m1)), ((r1 - 10, m1), ((r0 + 100) % 160, m0))]):
+        for r, mag in rows_mags:
+            big = torch.zeros(512 + 64)
+            big[:64] = mag
+            c[bq, r] = big.to(torch.bfloat16)
+        ql[bq, :, :, :64] = torch.ones(64).to(torch.bfloat16)
+    ref_o, ref_l = oracle_mod.mla(ql, qr, c, sl, shape.scale)
+    out, lse = run_mla(da, shape, (ql, qr, c, sl), workers)
+    compare(out, lse, ref_o, ref_l, "score jumps %s workers %d" % (pos, workers))
+
+
 # ------------------------------------------------------------------ MLA, full-size workloads, sampled rows
 def full_size_mla(da, oracle_mod, shape, n_rows=192):
     tensors = wl.make_mla(shape)
