@@ -1,7 +1,8 @@
 // Log-sum-exp combine of split-KV partial results.
 //
 // A sequence whose cache rows were split over several workers has one partial
-// (out_r normalized by its own softmax sum, lse_r in log2 units) per segment.
+// (out_r normalized by its own softmax sum and stored as bf16, lse_r in log2
+// units, fp32) per segment.
 // The merged result is lse = log(sum_r 2^lse_r) and out = sum_r 2^(lse_r - lse)
 // out_r, which equals softmax attention over the union of the segments' rows.
 // Empty segments carry lse_r = -inf and weigh nothing. Sequences with no cache
@@ -20,7 +21,7 @@ namespace da {
 template <int DV>
 __global__ void __launch_bounds__(256) combine_kernel(int B, int M, const PlanHeader *__restrict__ hdr,
                                                       const int *__restrict__ slot_start,
-                                                      const float *__restrict__ part_out,
+                                                      const uint16_t *__restrict__ part_out,
                                                       const float *__restrict__ part_lse,
                                                       uint16_t *__restrict__ out, float *__restrict__ lse)
 {
@@ -48,9 +49,18 @@ __global__ void __launch_bounds__(256) combine_kernel(int B, int M, const PlanHe
             for (int r = 0; r < nseg; ++r) {
                 const float wgt = fast_exp2(part_lse[(size_t)(s0 + r) * M + row] - m);
                 wsum += wgt;
-                const float *src = part_out + ((size_t)(s0 + r) * M + row) * DV + lane * CPL;
+                const uint16_t *src = part_out + ((size_t)(s0 + r) * M + row) * DV + lane * CPL;
+                if constexpr (CPL % 2 == 0) {
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) acc[c] += wgt * src[c];
+                    for (int c = 0; c < CPL / 2; ++c) {
+                        const uint32_t u = ((const uint32_t *)src)[c];
+                        acc[2 * c] += wgt * bf16lo_to_f32(u);
+                        acc[2 * c + 1] += wgt * bf16hi_to_f32(u);
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) acc[c] += wgt * bf16lo_to_f32(src[c]);
+                }
             }
         }
         const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

@@ -89,7 +89,7 @@ hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint1
     int *tile_start = (int *)(wsp + ws.tile_start);
     int *slot_start = (int *)(wsp + ws.slot_start);
     float *part_lse = (float *)(wsp + ws.part_lse);
-    float *part_out = (float *)(wsp + ws.part_out);
+    uint16_t *part_out = (uint16_t *)(wsp + ws.part_out);
 
     const int rb = mla_row_blocks(s, h);
     const int units = workers * rb;
@@ -165,7 +165,7 @@ bool gqa_valu_ok(int rows) { return rows <= 16; }
 template <int D, int R>
 void launch_gqa_valu(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *seqlens, int b, int s,
                      int hq, int hkv, int t_max, float scale_log2, uint16_t *out, float *lse, da::PlanHeader *hdr,
-                     int *tile_start, int *slot_start, float *part_out, float *part_lse, int workers,
+                     int *tile_start, int *slot_start, uint16_t *part_out, float *part_lse, int workers,
                      hipStream_t stream)
 {
     const int hb = gqa_head_blocks(hkv);
@@ -179,7 +179,7 @@ void launch_gqa_valu(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
 template <int D>
 bool dispatch_gqa_valu(int rows, const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *seqlens,
                        int b, int s, int hq, int hkv, int t_max, float scale_log2, uint16_t *out, float *lse,
-                       da::PlanHeader *hdr, int *tile_start, int *slot_start, float *part_out, float *part_lse,
+                       da::PlanHeader *hdr, int *tile_start, int *slot_start, uint16_t *part_out, float *part_lse,
                        int workers, hipStream_t stream)
 {
 #define DA_GQA_CASE(RR)                                                                                            \
@@ -199,7 +199,7 @@ bool dispatch_gqa_valu(int rows, const uint16_t *q, const uint16_t *k, const uin
 template <int D, int RBLK>
 hipError_t launch_gqa_mfma(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *seqlens, int b,
                            int s, int hq, int hkv, int t_max, float scale_log2, uint16_t *out, float *lse,
-                           da::PlanHeader *hdr, int *tile_start, int *slot_start, float *part_out, float *part_lse,
+                           da::PlanHeader *hdr, int *tile_start, int *slot_start, uint16_t *part_out, float *part_lse,
                            int workers, hipStream_t stream)
 {
     using C = GqaMfmaCfgFor<D, RBLK>;
@@ -223,7 +223,7 @@ template <int D>
 hipError_t dispatch_gqa_mfma(int rows, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                              const int32_t *seqlens, int b, int s, int hq, int hkv, int t_max, float scale_log2,
                              uint16_t *out, float *lse, da::PlanHeader *hdr, int *tile_start, int *slot_start,
-                             float *part_out, float *part_lse, int workers, hipStream_t stream)
+                             uint16_t *part_out, float *part_lse, int workers, hipStream_t stream)
 {
     if (rows <= 16)
         return launch_gqa_mfma<D, 1>(q, k, v, seqlens, b, s, hq, hkv, t_max, scale_log2, out, lse, hdr, tile_start,
@@ -357,7 +357,7 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
     int *tile_start = (int *)(wsp + ws.tile_start);
     int *slot_start = (int *)(wsp + ws.slot_start);
     float *part_lse = (float *)(wsp + ws.part_lse);
-    float *part_out = (float *)(wsp + ws.part_out);
+    uint16_t *part_out = (uint16_t *)(wsp + ws.part_out);
     hipStream_t st_ = (hipStream_t)stream;
     const float sl2 = scale * da::kLog2e;
 

@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(256)
                     int hkv, int t_max, float scale_log2, int head_blocks, int units,
                     PlanHeader *__restrict__ hdr, int *__restrict__ tile_start,
                     int *__restrict__ slot_start, uint16_t *__restrict__ out, float *__restrict__ lse,
-                    float *__restrict__ part_out, float *__restrict__ part_lse)
+                    uint16_t *__restrict__ part_out, float *__restrict__ part_lse)
 {
     using C = GqaValuCfg<D, R>;
     const int unit = xcd_linear_unit(blockIdx.x, gridDim.x);
@@ -131,18 +131,17 @@ __global__ void __launch_bounds__(256)
             const int row = row_of(r);
             const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
             const float lse2 = l[r] > 0.f ? m[r] + fast_log2(l[r]) : -INFINITY;
+            // the result, or this segment's bf16 partial for the combine
+            u32x4 v;
+            v[0] = pack_bf16x2(acc[r][0] * inv, acc[r][1] * inv);
+            v[1] = pack_bf16x2(acc[r][2] * inv, acc[r][3] * inv);
+            v[2] = pack_bf16x2(acc[r][4] * inv, acc[r][5] * inv);
+            v[3] = pack_bf16x2(acc[r][6] * inv, acc[r][7] * inv);
             if (direct) {
-                u32x4 v;
-                v[0] = pack_bf16x2(acc[r][0] * inv, acc[r][1] * inv);
-                v[1] = pack_bf16x2(acc[r][2] * inv, acc[r][3] * inv);
-                v[2] = pack_bf16x2(acc[r][4] * inv, acc[r][5] * inv);
-                v[3] = pack_bf16x2(acc[r][6] * inv, acc[r][7] * inv);
                 *(u32x4 *)(out + ((size_t)bq * M + row) * D + dg * 8) = v;
                 if (dg == 0) lse[(size_t)bq * M + row] = lse2 * kLn2;
             } else {
-                float *o = part_out + ((size_t)sl * M + row) * D + dg * 8;
-                *(f32x4 *)o = f32x4{acc[r][0] * inv, acc[r][1] * inv, acc[r][2] * inv, acc[r][3] * inv};
-                *(f32x4 *)(o + 4) = f32x4{acc[r][4] * inv, acc[r][5] * inv, acc[r][6] * inv, acc[r][7] * inv};
+                *(u32x4 *)(part_out + ((size_t)sl * M + row) * D + dg * 8) = v;
                 if (dg == 0) part_lse[(size_t)sl * M + row] = lse2;
             }
         }
@@ -334,7 +333,7 @@ __global__ void __launch_bounds__(64 * HPB, 1)
                     int hkv, int t_max, float scale_log2, int head_blocks, int units,
                     PlanHeader *__restrict__ hdr, int *__restrict__ tile_start,
                     int *__restrict__ slot_start, uint16_t *__restrict__ out, float *__restrict__ lse,
-                    float *__restrict__ part_out, float *__restrict__ part_lse)
+                    uint16_t *__restrict__ part_out, float *__restrict__ part_lse)
 {
     using C = GqaMfmaCfg<D, RBLK, HPB, NST>;
     constexpr int SUB = kGqaTile / C::T;  // stages per planner tile
@@ -449,21 +448,21 @@ __global__ void __launch_bounds__(64 * HPB, 1)
             const int row = row_of(r);
             const float inv = lsum[rb] > 0.f ? 1.f / lsum[rb] : 0.f;
             const float lse2 = lsum[rb] > 0.f ? mref[rb] + fast_log2(lsum[rb]) : -INFINITY;
-            if (nseg == 1) {
-                uint16_t *o = out + ((size_t)bq * M + row) * D + g * 4;
+            // the result, or this segment's bf16 partial for the combine
+            uint16_t *o = nseg == 1 ? out + ((size_t)bq * M + row) * D + g * 4
+                                    : part_out + ((size_t)sl * M + row) * D + g * 4;
 #pragma unroll
-                for (int db = 0; db < C::DB; ++db) {
-                    u32x2 v;
-                    v[0] = pack_bf16x2(acc[rb][db][0] * inv, acc[rb][db][1] * inv);
-                    v[1] = pack_bf16x2(acc[rb][db][2] * inv, acc[rb][db][3] * inv);
-                    *(u32x2 *)(o + db * 16) = v;
-                }
-                if (g == 0) lse[(size_t)bq * M + row] = lse2 * kLn2;
-            } else {
-                float *o = part_out + ((size_t)sl * M + row) * D + g * 4;
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db) *(f32x4 *)(o + db * 16) = acc[rb][db] * inv;
-                if (g == 0) part_lse[(size_t)sl * M + row] = lse2;
+            for (int db = 0; db < C::DB; ++db) {
+                u32x2 v;
+                v[0] = pack_bf16x2(acc[rb][db][0] * inv, acc[rb][db][1] * inv);
+                v[1] = pack_bf16x2(acc[rb][db][2] * inv, acc[rb][db][3] * inv);
+                *(u32x2 *)(o + db * 16) = v;
+            }
+            if (g == 0) {
+                if (nseg == 1)
+                    lse[(size_t)bq * M + row] = lse2 * kLn2;
+                else
+                    part_lse[(size_t)sl * M + row] = lse2;
             }
         }
     };

@@ -126,7 +126,7 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
                       const uint16_t *__restrict__ cache, const int32_t *__restrict__ seqlens, int B, int s,
                       int h, int t_max, float scale_log2, int row_blocks, int units,
                       PlanHeader *__restrict__ hdr, int *__restrict__ tile_start, int *__restrict__ slot_start,
-                      uint16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ part_out,
+                      uint16_t *__restrict__ out, float *__restrict__ lse, uint16_t *__restrict__ part_out,
                       float *__restrict__ part_lse)
 {
     using C = MlaCfg<K, P>;
@@ -491,13 +491,11 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
                     const int bq = cur.b;
                     const int nseg = cur.ns;
                     const int sl = cur.slot(worker);
+                    // the result, or this segment's bf16 partial for the combine
+                    uint16_t *const dst = nseg == 1 ? out + (size_t)bq * M * K : part_out + (size_t)sl * M * K;
                     auto put4 = [&](int row, int col, const f32x4 &v, float inv) {
-                        if (nseg == 1) {
-                            *(u32x2 *)(out + ((size_t)bq * M + row) * K + col) =
-                                u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
-                        } else {
-                            *(f32x4 *)(part_out + ((size_t)sl * M + row) * K + col) = v * inv;
-                        }
+                        *(u32x2 *)(dst + (size_t)row * K + col) =
+                            u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
                     };
 #pragma unroll
                     for (int r2 = 0; r2 < 2; ++r2) {

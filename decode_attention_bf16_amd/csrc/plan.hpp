@@ -50,8 +50,8 @@ static inline WsLayout ws_layout(int b, int rows_per_seq, int dv, int workers)
     off = align256(off + sizeof(int) * (size_t)(b + 1));
     w.part_lse = off;
     off = align256(off + sizeof(float) * (size_t)w.max_slots * rows_per_seq);
-    w.part_out = off;
-    off = align256(off + sizeof(float) * (size_t)w.max_slots * rows_per_seq * dv);
+    w.part_out = off;  // bf16 partial outputs, normalized by their own softmax sums
+    off = align256(off + sizeof(uint16_t) * (size_t)w.max_slots * rows_per_seq * dv);
     w.total = off;
     return w;
 }

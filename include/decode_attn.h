@@ -24,7 +24,11 @@
  *    drafts' own rows). A row that sees no cache row gets out = 0, lse = -inf.
  *  - lse is in natural-log units, fp32. out is bf16, rounded to nearest even.
  *  - Arithmetic: bf16 products with fp32 accumulation (MFMA / dot2), fp32
- *    online softmax. Results are not bitwise identical across split choices.
+ *    online softmax. A sequence split over several workers passes through
+ *    per-segment partial outputs normalized by their own softmax sums and
+ *    stored as bf16 (one extra rounding, as the final output's), with fp32
+ *    log-sum-exps, before its combine. Results are not bitwise identical
+ *    across split choices.
  *
  * Pointers and ownership
  *  - Every tensor pointer is a DEVICE pointer to contiguous row-major memory;
@@ -73,7 +77,7 @@ const char *da_status_string(da_status status);
  * workers; a sequence touched by several workers is merged afterwards by a
  * log-sum-exp combine. num_workers = 0 lets the library choose from the
  * device's compute-unit count and the shapes. Any value >= 1 is valid and
- * gives the same result up to fp32 rounding.
+ * gives the same result up to rounding (of the bf16 partials when split).
  */
 
 /*
@@ -119,7 +123,7 @@ size_t gqa_decode_workspace_size(int b, int s, int hq, int hkv, int d, int t_max
  * head with R <= 64 (R <= 32 for d = 256); t_max * hkv * d * 2 < 2^31.
  * `path` selects the kernel: 1 = VALU dot kernel (R <= 16), 2 = MFMA kernel
  * (rows padded to blocks of 16), 0 = automatic (currently the MFMA kernel for
- * every R). Both give the same result up to fp32 rounding.
+ * every R). Both give the same result up to rounding.
  */
 da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
                      const int32_t *seqlens, int b, int s, int hq, int hkv, int d, int t_max,

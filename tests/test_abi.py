@@ -119,7 +119,8 @@ def test_workspace_size_explicit_workers(lib):
     b, s, h, k, p, t, w = 32, 1, 128, 512, 64, 4096, 128
     sz = lib.mla_decode_workspace_size(b, s, h, k, p, t, w)
     slots = b + w
-    assert sz >= slots * s * h * (k + 1) * 4
-    assert sz < slots * s * h * (k + 1) * 4 + 64 * 1024
+    # per partial slot and query row: k bf16 outputs and one fp32 lse
+    assert sz >= slots * s * h * (2 * k + 4)
+    assert sz < slots * s * h * (2 * k + 4) + 64 * 1024
     # too-small workspace is reported as such (checked before any launch)
     assert mla_call(lib, b=b, s=s, h=h, t=t, nw=w, wsb=sz - 1, ws=ctypes.c_void_p(0x100000)) == DA_ERR_WORKSPACE
