@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="s-sweep of MLA (one JSON line per s)")
     ap.add_argument("--ragged", action="store_true", help="only the ragged long-context MLA workload")
+    ap.add_argument("--gqa-long", action="store_true",
+                    help="only the long-context GQA workload (t=262144, hq=24, hkv=4, d=256), both kernels")
     ap.add_argument("--only", default="", help="comma list of parts to run (gqa,mla_s1,mla_s4)")
     ap.add_argument("--gqa-path", type=int, default=0, help="GQA kernel: 0 auto, 1 VALU dot, 2 MFMA")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -195,6 +197,21 @@ def main():
                           "tbs": round(c.bytes / sec / 1e12, 3), "ai": round(c.ai, 1),
                           "bound": "mfma" if c.ai > RIDGE else "hbm", "t_min_us": round(t_min * 1e6, 2),
                           "roofline_frac": round(t_min / sec, 4)}), flush=True)
+        return
+
+    if args.gqa_long:
+        for path in (2, 1):
+            p = Part("gqa_long", "gqa", wl.GQA_LONG, dev, path=path)
+            wall, per = time_parts([p], args.steps, args.warmup)
+            sec = per[p.name]
+            c = p.cost
+            print(json.dumps({"workload": "gqa_long (b=1, s=1, hq=24, hkv=4, d=256, t=262144, seed 6)",
+                              "kernel": "mfma" if path == 2 else "valu",
+                              "us": round(sec * 1e6, 2), "tflops": round(c.flops / sec / 1e12, 3),
+                              "tbs": round(c.bytes / sec / 1e12, 3), "ai": round(c.ai, 1), "bound": p.bound,
+                              "t_min_us": round(p.t_min * 1e6, 2), "roofline_frac": round(p.t_min / sec, 4)}),
+                  flush=True)
+            del p
         return
 
     if args.sweep:

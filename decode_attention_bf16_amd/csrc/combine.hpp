@@ -2,18 +2,104 @@
 //
 // A sequence whose cache rows were split over several workers has one partial
 // (out_r normalized by its own softmax sum and stored as bf16, lse_r in log2
-// units, fp32) per segment.
-// The merged result is lse = log(sum_r 2^lse_r) and out = sum_r 2^(lse_r - lse)
-// out_r, which equals softmax attention over the union of the segments' rows.
-// Empty segments carry lse_r = -inf and weigh nothing. Sequences with no cache
-// row at all (no segment) get out = 0, lse = -inf here; sequences with a
-// single segment were written by their worker and are skipped.
+// units, fp32) per segment. The merged result is lse = log(sum_r 2^lse_r) and
+// out = sum_r 2^(lse_r - lse) out_r, which equals softmax attention over the
+// union of the segments' rows. Empty segments carry lse_r = -inf and weigh
+// nothing. Sequences with no cache row at all (no segment) get out = 0,
+// lse = -inf here; sequences with a single segment were written by their worker
+// and are skipped.
+//
+// Two launch shapes: combine_kernel gives each query row one wave (the usual
+// case, a few segments per row); combine_wide_kernel gives each row a block of
+// sixteen waves that split its segments (long sequences split over many
+// workers, where one wave walking a hundred segments would be latency-bound).
 #pragma once
 
 #include "common.hpp"
 #include "plan.hpp"
 
 namespace da {
+
+__device__ __forceinline__ float wave_max64(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+// This lane's CPL columns of segment partial `src` (bf16) as floats.
+template <int CPL>
+__device__ __forceinline__ void load_partial(const uint16_t *__restrict__ src, float (&o)[CPL])
+{
+    if constexpr (CPL % 2 == 0) {
+#pragma unroll
+        for (int c = 0; c < CPL / 2; ++c) {
+            const uint32_t u = ((const uint32_t *)src)[c];
+            o[2 * c] = bf16lo_to_f32(u);
+            o[2 * c + 1] = bf16hi_to_f32(u);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) o[c] = bf16lo_to_f32(src[c]);
+    }
+}
+
+// acc += sum over segments r = r0, r0 + step, ... < nseg of 2^(lse_r - m) out_r
+// (this lane's columns), wsum += the weights. Four segments per round, so
+// their loads are in flight together.
+template <int DV>
+__device__ __forceinline__ void combine_accumulate(const uint16_t *__restrict__ part_out,
+                                                   const float *__restrict__ part_lse, int M, int row, int s0,
+                                                   int r0, int step, int nseg, float m, int lane,
+                                                   float (&acc)[DV / 64], float &wsum)
+{
+    constexpr int CPL = DV / 64;
+    auto src = [&](int r) { return part_out + ((size_t)(s0 + r) * M + row) * DV + lane * CPL; };
+    auto lse_of = [&](int r) { return part_lse[(size_t)(s0 + r) * M + row]; };
+    int r = r0;
+    for (; r + 3 * step < nseg; r += 4 * step) {
+        float wr[4], o[4][CPL];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            wr[u] = lse_of(r + u * step);
+            load_partial<CPL>(src(r + u * step), o[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float wgt = fast_exp2(wr[u] - m);
+            wsum += wgt;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[c] += wgt * o[u][c];
+        }
+    }
+    for (; r < nseg; r += step) {
+        float o[CPL];
+        const float wgt = fast_exp2(lse_of(r) - m);
+        load_partial<CPL>(src(r), o);
+        wsum += wgt;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] += wgt * o[c];
+    }
+}
+
+// The merged row: out (bf16) and lse (natural log).
+template <int DV>
+__device__ __forceinline__ void combine_write(uint16_t *__restrict__ out, float *__restrict__ lse, long row_g, int lane,
+                                              const float (&acc)[DV / 64], float wsum, float m)
+{
+    constexpr int CPL = DV / 64;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    if constexpr (CPL % 2 == 0) {
+        uint32_t *dst = (uint32_t *)(out + (size_t)row_g * DV + lane * CPL);
+#pragma unroll
+        for (int c = 0; c < CPL / 2; ++c) dst[c] = pack_bf16x2(acc[2 * c] * inv, acc[2 * c + 1] * inv);
+    } else {
+        uint16_t *dst = out + (size_t)row_g * DV + lane * CPL;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) dst[c] = to_bf16_bits(acc[c] * inv);
+    }
+    if (lane == 0) lse[row_g] = wsum > 0.f ? (m + fast_log2(wsum)) * kLn2 : -INFINITY;
+}
 
 // One wave per query row (grid-stride over rows); DV output columns spread
 // over the 64 lanes. A launch of a few blocks per CU keeps the cost low when
@@ -27,7 +113,6 @@ __global__ void __launch_bounds__(256) combine_kernel(int B, int M, const PlanHe
 {
     static_assert(DV % 64 == 0, "whole columns per lane");
     if (hdr->merge_seqs == 0) return;  // every sequence was written by its one worker
-    constexpr int CPL = DV / 64;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const long rows = (long)B * M;
@@ -39,51 +124,93 @@ __global__ void __launch_bounds__(256) combine_kernel(int B, int M, const PlanHe
         if (nseg == 1) continue;
 
         float m = -INFINITY;
-        for (int r = 0; r < nseg; ++r) m = fmaxf(m, part_lse[(size_t)(s0 + r) * M + row]);
+        for (int r = lane; r < nseg; r += 64) m = fmaxf(m, part_lse[(size_t)(s0 + r) * M + row]);
+        m = wave_max64(m);
+        float acc[DV / 64];
+#pragma unroll
+        for (int c = 0; c < DV / 64; ++c) acc[c] = 0.f;
+        float wsum = 0.f;
+        if (m != -INFINITY) combine_accumulate<DV>(part_out, part_lse, M, row, s0, 0, 1, nseg, m, lane, acc, wsum);
+        combine_write<DV>(out, lse, row_g, lane, acc, wsum, m);
+    }
+}
+
+// One block of sixteen waves per query row (grid-stride over rows): the waves
+// take the row's segments in turn and their sums meet in LDS.
+constexpr int kCombineWideWaves = 16;
+
+template <int DV>
+__global__ void __launch_bounds__(64 * kCombineWideWaves) combine_wide_kernel(
+    int B, int M, const PlanHeader *__restrict__ hdr, const int *__restrict__ slot_start,
+    const uint16_t *__restrict__ part_out, const float *__restrict__ part_lse, uint16_t *__restrict__ out,
+    float *__restrict__ lse)
+{
+    constexpr int NW = kCombineWideWaves, CPL = DV / 64;
+    if (hdr->merge_seqs == 0) return;
+    __shared__ float red_m[NW];
+    __shared__ float red_w[NW];
+    __shared__ float red_acc[NW][DV];  // [wave][column-in-lane c * 64 + lane]
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const long rows = (long)B * M;
+    for (long row_g = blockIdx.x; row_g < rows; row_g += gridDim.x) {
+        const int bq = (int)(row_g / M);
+        const int row = (int)(row_g - (long)bq * M);
+        const int s0 = slot_start[bq];
+        const int nseg = slot_start[bq + 1] - s0;
+        if (nseg == 1) continue;  // the same for the whole block
+
+        float m = -INFINITY;
+        for (int r = threadIdx.x; r < nseg; r += 64 * NW) m = fmaxf(m, part_lse[(size_t)(s0 + r) * M + row]);
+        m = wave_max64(m);
+        if (lane == 0) red_m[wave] = m;
+        __syncthreads();
+        m = red_m[0];
+#pragma unroll
+        for (int w2 = 1; w2 < NW; ++w2) m = fmaxf(m, red_m[w2]);
 
         float acc[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
         float wsum = 0.f;
-        if (m != -INFINITY) {
-            for (int r = 0; r < nseg; ++r) {
-                const float wgt = fast_exp2(part_lse[(size_t)(s0 + r) * M + row] - m);
-                wsum += wgt;
-                const uint16_t *src = part_out + ((size_t)(s0 + r) * M + row) * DV + lane * CPL;
-                if constexpr (CPL % 2 == 0) {
+        if (m != -INFINITY)
+            combine_accumulate<DV>(part_out, part_lse, M, row, s0, wave, NW, nseg, m, lane, acc, wsum);
 #pragma unroll
-                    for (int c = 0; c < CPL / 2; ++c) {
-                        const uint32_t u = ((const uint32_t *)src)[c];
-                        acc[2 * c] += wgt * bf16lo_to_f32(u);
-                        acc[2 * c + 1] += wgt * bf16hi_to_f32(u);
-                    }
-                } else {
+        for (int c = 0; c < CPL; ++c) red_acc[wave][c * 64 + lane] = acc[c];
+        if (lane == 0) red_w[wave] = wsum;
+        __syncthreads();
+        if (wave == 0) {
+            float tot[CPL];
+            float ws = 0.f;
 #pragma unroll
-                    for (int c = 0; c < CPL; ++c) acc[c] += wgt * bf16lo_to_f32(src[c]);
-                }
+            for (int c = 0; c < CPL; ++c) tot[c] = 0.f;
+            for (int w2 = 0; w2 < NW; ++w2) {
+                ws += red_w[w2];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) tot[c] += red_acc[w2][c * 64 + lane];
             }
+            combine_write<DV>(out, lse, row_g, lane, tot, ws, m);
         }
-        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-        if constexpr (CPL % 2 == 0) {
-            uint32_t *dst = (uint32_t *)(out + (size_t)row_g * DV + lane * CPL);
-#pragma unroll
-            for (int c = 0; c < CPL / 2; ++c) dst[c] = pack_bf16x2(acc[2 * c] * inv, acc[2 * c + 1] * inv);
-        } else {
-            uint16_t *dst = out + (size_t)row_g * DV + lane * CPL;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) dst[c] = to_bf16_bits(acc[c] * inv);
-        }
-        if (lane == 0) lse[row_g] = wsum > 0.f ? (m + fast_log2(wsum)) * kLn2 : -INFINITY;
+        __syncthreads();  // red_* are reused by the next row
     }
 }
 
-// Blocks of the combine launch: enough to cover the rows with a few waves per
-// CU, never more than one block per four rows.
+// Blocks of the one-wave-per-row launch: enough to cover the rows with a few
+// waves per CU, never more than one block per four rows.
 inline unsigned combine_grid(long rows, int cus)
 {
     const long want = (long)cus * 4;
     const long need = (rows + 3) / 4;
     return (unsigned)(need < want ? (need > 0 ? need : 1) : want);
+}
+
+// Whether a split over `workers` workers leaves the b sequences more than 16
+// segments each on average: then the combine gives each row a block.
+inline bool combine_use_wide(int b, int workers) { return (long)b + workers > 16L * b; }
+
+inline unsigned combine_wide_grid(long rows, int cus)
+{
+    return (unsigned)(rows < cus ? (rows > 0 ? rows : 1) : cus);
 }
 
 }  // namespace da

@@ -40,6 +40,23 @@ int current_cu_count()
     return g_dev[dev].cu_count;
 }
 
+// The log-sum-exp combine for DV-wide rows (one wave per row, or a block per
+// row when the sequences average more than 16 segments).
+template <int DV>
+void launch_combine(int b, int M, int workers, da::PlanHeader *hdr, const int *slot_start, const uint16_t *part_out,
+                    const float *part_lse, uint16_t *out, float *lse, hipStream_t stream)
+{
+    const long rows = (long)b * M;
+    const int cus = current_cu_count();
+    if (da::combine_use_wide(b, workers))
+        hipLaunchKernelGGL(da::combine_wide_kernel<DV>, dim3(da::combine_wide_grid(rows, cus)),
+                           dim3(64 * da::kCombineWideWaves), 0, stream, b, M, hdr, slot_start, part_out, part_lse, out,
+                           lse);
+    else
+        hipLaunchKernelGGL(da::combine_kernel<DV>, dim3(da::combine_grid(rows, cus)), dim3(256), 0, stream, b, M, hdr,
+                           slot_start, part_out, part_lse, out, lse);
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool log_plan()
@@ -100,9 +117,7 @@ hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint1
     hipLaunchKernelGGL((da::mla_decode_kernel<K, P>), dim3(grid), dim3(C::THREADS), C::LDS_BYTES, stream, q_lat, q_rope,
                        cache, seqlens, b, s, h, t_max, scale_log2, rb, units, hdr, tile_start, slot_start, out, lse,
                        part_out, part_lse);
-    const long rows = (long)b * s * h;
-    hipLaunchKernelGGL(da::combine_kernel<K>, dim3(da::combine_grid(rows, current_cu_count())), dim3(256), 0, stream, b, s * h,
-                       hdr, slot_start, part_out, part_lse, out, lse);
+    launch_combine<K>(b, s * h, workers, hdr, slot_start, part_out, part_lse, out, lse, stream);
     return hipGetLastError();
 }
 
@@ -388,16 +403,12 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
         ok = dispatch_gqa_valu<256>(rows, q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
                                     tile_start, slot_start, part_out, part_lse, workers, st_);
     if (!ok) return DA_ERR_UNSUPPORTED;
-    const long nrows = (long)b * s * hq;
     if (d == 64)
-        hipLaunchKernelGGL(da::combine_kernel<64>, dim3(da::combine_grid(nrows, current_cu_count())), dim3(256), 0, st_, b, s * hq,
-                           hdr, slot_start, part_out, part_lse, out, lse);
+        launch_combine<64>(b, s * hq, workers, hdr, slot_start, part_out, part_lse, out, lse, st_);
     else if (d == 128)
-        hipLaunchKernelGGL(da::combine_kernel<128>, dim3(da::combine_grid(nrows, current_cu_count())), dim3(256), 0, st_, b, s * hq,
-                           hdr, slot_start, part_out, part_lse, out, lse);
+        launch_combine<128>(b, s * hq, workers, hdr, slot_start, part_out, part_lse, out, lse, st_);
     else
-        hipLaunchKernelGGL(da::combine_kernel<256>, dim3(da::combine_grid(nrows, current_cu_count())), dim3(256), 0, st_, b, s * hq,
-                           hdr, slot_start, part_out, part_lse, out, lse);
+        launch_combine<256>(b, s * hq, workers, hdr, slot_start, part_out, part_lse, out, lse, st_);
     return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

@@ -137,6 +137,21 @@ def test_mla_all_sequences_empty(da, workers):
     assert torch.all(torch.isneginf(lse))
 
 
+@pytest.mark.parametrize("case", [(2, 1, 128, 512, 64, 3000, [3000, 1700], 120),
+                                  (3, 2, 16, 64, 16, 900, [900, 0, 33], 100),
+                                  (1, 4, 32, 256, 64, 2000, [1999], 64)],
+                         ids=lambda c: "b%d_s%d_k%d_w%d" % (c[0], c[1], c[3], c[7]))
+def test_mla_many_segments_per_row(da, oracle_mod, case):
+    """Few sequences split over many workers (more than 16 segments per
+    sequence on average): the combine gives each row a block of waves."""
+    b, s, h, k, p, t, sl, workers = case
+    shape = mla_shape(b, s, h, k, p, t, seed=200 + b + workers)
+    tensors = wl.make_mla(shape, seqlens=sl)
+    out, lse = run_mla(da, shape, tensors, workers)
+    ref_o, ref_l = oracle_mod.mla(*tensors, shape.scale)
+    compare(out, lse, ref_o, ref_l, "mla many segments %s" % (case,))
+
+
 def test_mla_split_counts_agree(da):
     shape = mla_shape(4, 2, 64, 512, 64, 700, seed=7)
     tensors = wl.make_mla(shape, seqlens=[700, 511, 65, 300])
@@ -267,6 +282,7 @@ GQA_SMALL = [
     (1, 4, 32, 4, 256, 64, [64]),            # d = 256, 32 rows
     (2, 1, 10, 5, 128, 90, [90, 40]),        # 5 KV heads: the second head block has one active wave
     (2, 2, 18, 9, 64, 80, [80, 3]),          # d = 64, 9 KV heads over two head blocks
+    (2, 2, 24, 4, 256, 150, [150, 77]),      # groups of 6 at d = 256 (12 rows per KV head)
 ]
 
 
@@ -319,6 +335,41 @@ def test_gqa_layer_full_size(da, oracle_mod, path):
     rows = wl.sample_rows(shape.rows, 512, shape.seed).numpy()
     ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale, rows=rows)
     compare(out.reshape(-1, shape.d)[rows], lse.reshape(-1)[rows], ref_o, ref_l, "gqa full path=%d" % path)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("case", [(2, 1, 24, 4, 256, 4000, [4000, 2500], 60),
+                                  (1, 2, 16, 2, 128, 3000, [3000], 40),
+                                  (2, 1, 8, 1, 64, 2048, [2048, 0], 50)],
+                         ids=lambda c: "b%d_s%d_d%d_w%d" % (c[0], c[1], c[4], c[7]))
+def test_gqa_many_segments_per_row(da, oracle_mod, case, path):
+    """Few sequences split over many workers: the combine's block-per-row form."""
+    b, s, hq, hkv, d, t, sl, workers = case
+    shape = wl.GQAShape(b=b, s=s, hq=hq, hkv=hkv, d=d, t_max=t, scale=1.0 / math.sqrt(d), seed=300 + workers)
+    tensors = wl.make_gqa(shape, seqlens=sl)
+    out, lse = run_gqa(da, shape, tensors, workers, path)
+    ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale)
+    compare(out, lse, ref_o, ref_l, "gqa many segments %s path %d" % (case, path))
+
+
+@pytest.fixture(scope="module")
+def gqa_long_case(oracle_mod):
+    """One 262,144-token sequence at 24 query / 4 KV heads, d = 256, with the
+    oracle's result for all 24 query rows (computed once for both paths)."""
+    shape = wl.GQA_LONG
+    tensors = wl.make_gqa(shape)
+    ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale)
+    return shape, tensors, ref_o, ref_l
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_gqa_long_context_groups_of_six(da, gqa_long_case, path):
+    shape, tensors, ref_o, ref_l = gqa_long_case
+    print("gqa long context (t=%d, hq=%d, hkv=%d, d=%d) path %d" % (shape.t_max, shape.hq, shape.hkv, shape.d, path),
+          flush=True)
+    out, lse = run_gqa(da, shape, tensors, 0, path)
+    compare(out.reshape(-1, shape.d), lse.reshape(-1), ref_o.reshape(-1, shape.d), ref_l.reshape(-1),
+            "gqa long path=%d" % path)
 
 
 @pytest.mark.parametrize("path", [1, 2])

@@ -66,6 +66,10 @@ MLA_MTP4 = MLAShape(b=32, s=4, h=128, k=512, p=64, t_max=4096, scale=1.0 / math.
 MLA_RAGGED = MLAShape(b=64, s=1, h=128, k=512, p=64, t_max=32768, scale=1.0 / math.sqrt(192), seed=4,
                       ragged=(1024, 32768))
 MTP_SWEEP = (1, 2, 4, 8, 16, 32)
+# The grouped geometry of the "MQA, GQA & MLA" lesson ("01 · Concept": 24 query heads in 4 groups of 6,
+# head dimension 256) at that page's full context: its 16 GiB per sequence over 16 caching layers at
+# 4 KiB per token per layer is 262,144 tokens. One sequence, one layer: K and V are 512 MiB each.
+GQA_LONG = GQAShape(b=1, s=1, hq=24, hkv=4, d=256, t_max=262144, scale=1.0 / 16.0, seed=6)
 
 
 def mla_mtp(s: int) -> MLAShape:
