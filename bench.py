@@ -20,6 +20,7 @@ sample of the same rows.
 from __future__ import annotations
 
 import argparse
+import math
 import hashlib
 import json
 import os
@@ -94,6 +95,34 @@ class Part:
         return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(a / PEAK_GBS, 4)}
 
 
+class UnabsorbedPart:
+    """One un-absorbed (per-head K/V) MLA decode call at the DeepSeek-V3-like shapes with s drafts. The
+    decompressed K [b,t,h,192] and V [b,t,h,128] (10.7 GB at b=32, t=4096) are drawn on the GPU from a
+    seeded generator and shared by every s."""
+
+    kv = None
+
+    def __init__(self, s, dev, b=32, h=128, t=4096):
+        self.name, self.s = "mla_unabsorbed_s%d" % s, s
+        if UnabsorbedPart.kv is None:
+            g = torch.Generator(device=dev).manual_seed(7)
+            UnabsorbedPart.kv = (torch.randn((b, t, h, 192), generator=g, device=dev, dtype=torch.bfloat16),
+                                 torch.randn((b, t, h, 128), generator=g, device=dev, dtype=torch.bfloat16),
+                                 torch.full((b,), t, dtype=torch.int32, device=dev))
+        g = torch.Generator(device=dev).manual_seed(100 + s)
+        self.q = torch.randn((b, s, h, 192), generator=g, device=dev, dtype=torch.bfloat16)
+        self.scale = 1.0 / math.sqrt(192)
+        self.out = torch.empty((b, s, h, 128), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
+        nbytes = binding.mla_decode_unabsorbed_workspace_size(b, s, h, 192, 128, t)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.cost = cm.mla_unabsorbed(b, h, s, t, 128, 64)
+
+    def __call__(self):
+        k, v, sl = UnabsorbedPart.kv
+        binding.mla_decode_unabsorbed(self.q, k, v, sl, self.scale, out=self.out, lse=self.lse, workspace=self.ws)
+
+
 def time_parts(parts, steps, warmup):
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -158,6 +187,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="s-sweep of MLA (one JSON line per s)")
     ap.add_argument("--ragged", action="store_true", help="only the ragged long-context MLA workload")
+    ap.add_argument("--crossover", action="store_true",
+                    help="absorbed vs un-absorbed MLA decode over the s-sweep (b=32, h=128, t=4096)")
     ap.add_argument("--gqa-long", action="store_true",
                     help="only the long-context GQA workload (t=262144, hq=24, hkv=4, d=256), both kernels")
     ap.add_argument("--only", default="", help="comma list of parts to run (gqa,mla_s1,mla_s4)")
@@ -197,6 +228,27 @@ def main():
                           "tbs": round(c.bytes / sec / 1e12, 3), "ai": round(c.ai, 1),
                           "bound": "mfma" if c.ai > RIDGE else "hbm", "t_min_us": round(t_min * 1e6, 2),
                           "roofline_frac": round(t_min / sec, 4)}), flush=True)
+        return
+
+    if args.crossover:
+        first = None
+        for s in wl.MTP_SWEEP + (48, 64):
+            pa = Part("mla_s%d" % s, "mla", wl.mla_mtp(s), dev)
+            pu = UnabsorbedPart(s, dev)
+            _, per = time_parts([pa, pu], args.steps, args.warmup)
+            ta, tu = per[pa.name], per[pu.name]
+            if first is None and tu < ta:
+                first = s
+            print(json.dumps({"crossover": "mla absorbed vs un-absorbed (b=32, h=128, t=4096, k=512, p=64, d=128)",
+                              "s": s, "absorbed_us": round(ta * 1e6, 2), "unabsorbed_us": round(tu * 1e6, 2),
+                              "absorbed_tflops": round(pa.cost.flops / ta / 1e12, 2),
+                              "unabsorbed_tflops": round(pu.cost.flops / tu / 1e12, 2),
+                              "unabsorbed_tbs": round(pu.cost.bytes / tu / 1e12, 3),
+                              "unabsorbed_roofline_frac": round(cm.roofline_time(pu.cost) / tu, 4),
+                              "faster": "unabsorbed" if tu < ta else "absorbed"}), flush=True)
+            del pa, pu
+        print(json.dumps({"crossover_s": first, "note": "smallest s of the sweep at which the un-absorbed kernel "
+                          "is faster (null: none up to s=64)"}), flush=True)
         return
 
     if args.gqa_long:

@@ -23,7 +23,8 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dimensions", 3: "work
            4: "HIP launch error"}
 
 EXPORTED = ("da_version", "da_status_string", "mla_decode_workspace_size", "mla_decode",
-            "gqa_decode_workspace_size", "gqa_decode")
+            "gqa_decode_workspace_size", "gqa_decode", "mla_decode_unabsorbed_workspace_size",
+            "mla_decode_unabsorbed")
 
 
 class DecodeAttentionError(RuntimeError):
@@ -58,6 +59,10 @@ def load_library():
         lib.gqa_decode_workspace_size.restype = Z
         lib.gqa_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, I, P]
         lib.gqa_decode.restype = I
+        lib.mla_decode_unabsorbed_workspace_size.argtypes = [I] * 7
+        lib.mla_decode_unabsorbed_workspace_size.restype = Z
+        lib.mla_decode_unabsorbed.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, P]
+        lib.mla_decode_unabsorbed.restype = I
         _lib = lib
         return lib
 
@@ -97,6 +102,10 @@ def mla_decode_workspace_size(b, s, h, k, p, t_max, num_workers=0) -> int:
 
 def gqa_decode_workspace_size(b, s, hq, hkv, d, t_max, num_workers=0, path=0) -> int:
     return int(load_library().gqa_decode_workspace_size(b, s, hq, hkv, d, t_max, num_workers, path))
+
+
+def mla_decode_unabsorbed_workspace_size(b, s, h, dqk, dv, t_max, num_workers=0) -> int:
+    return int(load_library().mla_decode_unabsorbed_workspace_size(b, s, h, dqk, dv, t_max, num_workers))
 
 
 def _workspace(nbytes, device, workspace):
@@ -180,4 +189,40 @@ def gqa_decode(q, k_cache, v_cache, seqlens, scale, num_workers=0, path=0, out=N
                             float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                             int(num_workers), int(path), _stream(dev))
     _check("gqa_decode", rc)
+    return out, lse
+
+
+def mla_decode_unabsorbed(q, k_cache, v_cache, seqlens, scale, num_workers=0, out=None, lse=None, workspace=None):
+    """Un-absorbed MLA decode on the GPU: per-head decompressed keys and values.
+
+    q [b,s,h,dqk], k_cache [b,t_max,h,dqk], v_cache [b,t_max,h,dv] (bf16), seqlens [b] (int32).
+    Returns (out [b,s,h,dv] bf16, lse [b,s,h] fp32).
+    """
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(seqlens, "seqlens", torch.int32, 1, dev)
+    b, s, h, dqk = q.shape
+    t_max, dv = k_cache.shape[1], v_cache.shape[3]
+    if tuple(k_cache.shape) != (b, t_max, h, dqk) or tuple(v_cache.shape) != (b, t_max, h, dv):
+        raise ValueError("k_cache must be [b, t_max, h, dqk] and v_cache [b, t_max, h, dv]")
+    if seqlens.shape[0] != b:
+        raise ValueError("seqlens must have b=%d entries" % b)
+    if out is None:
+        out = torch.empty((b, s, h, dv), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, 4, dev)
+    if lse is None:
+        lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
+    else:
+        _need(lse, "lse", torch.float32, 3, dev)
+    nbytes = lib.mla_decode_unabsorbed_workspace_size(b, s, h, dqk, dv, t_max, num_workers)
+    ws = _workspace(nbytes, dev, workspace)
+    with torch.cuda.device(dev):
+        rc = lib.mla_decode_unabsorbed(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), b, s, h, dqk, dv, t_max,
+                                       float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                       int(num_workers), _stream(dev))
+    _check("mla_decode_unabsorbed", rc)
     return out, lse

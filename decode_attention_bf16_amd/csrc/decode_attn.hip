@@ -259,6 +259,52 @@ int gqa_choose_path(int rows, int path)
     return 1;  // measured faster at every row count (see the design notes)
 }
 
+// ------------------------------------------------------------------ un-absorbed MLA
+// The grouped MFMA kernel with one query head per KV head (g = 1): per-head
+// key rows of 192 (128 decompressed + 64 rope) and value rows of 128.
+constexpr int kUnabsDK = 192, kUnabsDV = 128, kUnabsHPB = 2, kUnabsNST = 4;
+template <int RBLK>
+using UnabsCfg = da::GqaMfmaCfg<kUnabsDK, RBLK, kUnabsHPB, kUnabsNST, kUnabsDV>;
+
+int unabs_workers(int b, int h, int t_max, int requested)
+{
+    if (requested > 0) return requested;
+    int per_cu = 163840 / UnabsCfg<1>::LDS_BYTES;
+    if (per_cu < 1) per_cu = 1;
+    int w = per_cu * current_cu_count() / ((h + kUnabsHPB - 1) / kUnabsHPB);
+    if (w < 1) w = 1;
+    const long max_tiles = (long)b * ((t_max + da::kGqaTile - 1) / da::kGqaTile);
+    if ((long)w > max_tiles) w = (int)max_tiles;
+    return w < 1 ? 1 : w;
+}
+
+template <int RBLK>
+hipError_t launch_unabs(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *seqlens, int b, int s,
+                        int h, int t_max, float scale_log2, uint16_t *out, float *lse, da::PlanHeader *hdr,
+                        int *tile_start, int *slot_start, uint16_t *part_out, float *part_lse, int workers,
+                        hipStream_t stream)
+{
+    using C = UnabsCfg<RBLK>;
+    static std::once_flag attr_once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(attr_once, [] {
+        attr_err = hipFuncSetAttribute(
+            (const void *)da::gqa_mfma_kernel<kUnabsDK, RBLK, kUnabsHPB, kUnabsNST, kUnabsDV>,
+            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    const int hb = (h + C::HPB - 1) / C::HPB;
+    const int units = workers * hb;
+    const int grid = (units + 7) / 8 * 8;
+    if (log_plan())
+        fprintf(stderr, "[decode_attn] mla-unabsorbed b=%d s=%d h=%d t_max=%d workers=%d grid=%d lds=%d\n", b, s, h,
+                t_max, workers, grid, C::LDS_BYTES);
+    hipLaunchKernelGGL((da::gqa_mfma_kernel<kUnabsDK, RBLK, kUnabsHPB, kUnabsNST, kUnabsDV>), dim3(grid),
+                       dim3(C::THREADS), C::LDS_BYTES, stream, q, k, v, seqlens, b, s, h, h, t_max, scale_log2, hb,
+                       units, hdr, tile_start, slot_start, out, lse, part_out, part_lse);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -409,6 +455,61 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
         launch_combine<128>(b, s * hq, workers, hdr, slot_start, part_out, part_lse, out, lse, st_);
     else
         launch_combine<256>(b, s * hq, workers, hdr, slot_start, part_out, part_lse, out, lse, st_);
+    return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+static da_status unabs_check(int b, int s, int h, int dqk, int dv, int t_max, int num_workers)
+{
+    if (b <= 0 || s <= 0 || h <= 0 || dqk <= 0 || dv <= 0 || t_max <= 0 || num_workers < 0) return DA_ERR_INVALID_ARG;
+    if (s > t_max) return DA_ERR_INVALID_ARG;
+    if (!(dqk == kUnabsDK && dv == kUnabsDV)) return DA_ERR_UNSUPPORTED;
+    if (s > 64) return DA_ERR_UNSUPPORTED;
+    // one sequence's K rows must be addressable by a 32-bit buffer offset
+    if ((long long)t_max * h * dqk * 2 >= (1LL << 31)) return DA_ERR_UNSUPPORTED;
+    return DA_OK;
+}
+
+size_t mla_decode_unabsorbed_workspace_size(int b, int s, int h, int dqk, int dv, int t_max, int num_workers)
+{
+    if (unabs_check(b, s, h, dqk, dv, t_max, num_workers) != DA_OK) return 0;
+    return da::ws_layout(b, s * h, dv, unabs_workers(b, h, t_max, num_workers)).total;
+}
+
+da_status mla_decode_unabsorbed(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                                const int32_t *seqlens, int b, int s, int h, int dqk, int dv, int t_max, float scale,
+                                uint16_t *out, float *lse, void *workspace, size_t workspace_bytes, int num_workers,
+                                void *stream)
+{
+    da_status st = unabs_check(b, s, h, dqk, dv, t_max, num_workers);
+    if (st != DA_OK) return st;
+    if (!q || !k_cache || !v_cache || !seqlens || !out || !lse || !workspace) return DA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return DA_ERR_INVALID_ARG;
+    if (((uintptr_t)workspace & 255u) != 0) return DA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return DA_ERR_INVALID_ARG;
+    const int workers = unabs_workers(b, h, t_max, num_workers);
+    const da::WsLayout ws = da::ws_layout(b, s * h, dv, workers);
+    if (workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
+
+    char *wsp = (char *)workspace;
+    auto *hdr = (da::PlanHeader *)(wsp + ws.header);
+    int *tile_start = (int *)(wsp + ws.tile_start);
+    int *slot_start = (int *)(wsp + ws.slot_start);
+    float *part_lse = (float *)(wsp + ws.part_lse);
+    uint16_t *part_out = (uint16_t *)(wsp + ws.part_out);
+    hipStream_t st_ = (hipStream_t)stream;
+    const float sl2 = scale * da::kLog2e;
+    hipError_t e;
+    if (s <= 16)
+        e = launch_unabs<1>(q, k_cache, v_cache, seqlens, b, s, h, t_max, sl2, out, lse, hdr, tile_start, slot_start,
+                            part_out, part_lse, workers, st_);
+    else if (s <= 32)
+        e = launch_unabs<2>(q, k_cache, v_cache, seqlens, b, s, h, t_max, sl2, out, lse, hdr, tile_start, slot_start,
+                            part_out, part_lse, workers, st_);
+    else
+        e = launch_unabs<4>(q, k_cache, v_cache, seqlens, b, s, h, t_max, sl2, out, lse, hdr, tile_start, slot_start,
+                            part_out, part_lse, workers, st_);
+    if (e != hipSuccess) return DA_ERR_HIP;
+    launch_combine<kUnabsDV>(b, s * h, workers, hdr, slot_start, part_out, part_lse, out, lse, st_);
     return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

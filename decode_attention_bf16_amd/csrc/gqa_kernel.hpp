@@ -294,24 +294,31 @@ __device__ __forceinline__ void wait_stage_copies(int later)
     }
 }
 
-template <int D, int RBLK, int HPB_ = 512 / D, int NST_ = 4>
+// D: width of the query and key rows (the score dot products); DV: width of
+// the value and output rows (D unless the keys carry extra columns, as the
+// un-absorbed MLA form's decoupled rope part does).
+template <int D, int RBLK, int HPB_ = 512 / D, int NST_ = 4, int DV_ = D>
 struct GqaMfmaCfg {
-    static_assert(D == 64 || D == 128 || D == 256, "head dim");
+    static constexpr int DK = D, DV = DV_;
+    static_assert((DK == 64 || DK == 128 || DK == 192 || DK == 256) && (DV == 64 || DV == 128 || DV == 256),
+                  "head dims");
     static constexpr int HPB = HPB_;             // KV heads (waves) per block
-    static_assert(HPB >= 1 && HPB * D <= 512, "token row of the block's heads fits 1 KB");
+    static_assert(HPB >= 1 && HPB * DK <= 512 && HPB * DV <= 512, "token rows of the block's heads fit 1 KB");
     static constexpr int THREADS = 64 * HPB;
     static constexpr int T = 16;                 // tokens per stage
-    static constexpr int ROWB = HPB * D * 2;     // bytes of one token row (HPB heads x d)
-    static constexpr int STAGE_BYTES = 2 * T * ROWB;
+    static constexpr int ROWK = HPB * DK * 2;    // bytes of one K token row (HPB heads x DK)
+    static constexpr int ROWV = HPB * DV * 2;    // bytes of one V token row
+    static_assert(ROWK % 256 == 0 && ROWV % 256 == 0, "token rows are whole 16-chunk swizzle groups");
+    static constexpr int KCH = T * ROWK / 16;    // 16-byte chunks of a stage's K rows
+    static_assert(KCH % 64 == 0, "the K rows fill whole copy instructions");
+    static constexpr int STAGE_BYTES = T * (ROWK + ROWV);
     static constexpr int NST = NST_;             // ring depth (NST - 1 stages in flight)
     static constexpr int LDS_BYTES = NST * STAGE_BYTES;
-    static constexpr int RPC = 1024 / ROWB;      // token rows per 1 KB copy instruction
-    static constexpr int LPR = ROWB / 16;        // lanes per token row
     static constexpr int LW = STAGE_BYTES / 1024 / HPB;  // copy instructions per wave per stage
     static_assert(LW * HPB * 1024 == STAGE_BYTES, "stage splits into whole copies per wave");
     static_assert((NST - 2) * LW <= 63, "outstanding copies fit the vmcnt counter");
-    static constexpr int KS = D / 32;            // score k-steps
-    static constexpr int DB = D / 16;            // 16-wide output blocks
+    static constexpr int KS = DK / 32;           // score k-steps
+    static constexpr int DB = DV / 16;           // 16-wide output blocks
 };
 
 // XOR applied to the chunk index (low four bits) of token row t of a stage. A
@@ -326,7 +333,7 @@ __device__ __forceinline__ int gqa_swz(int t)
 }
 
 
-template <int D, int RBLK, int HPB, int NST>
+template <int D, int RBLK, int HPB, int NST, int DV = D>
 __global__ void __launch_bounds__(64 * HPB, 1)
     gqa_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
                     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens, int B, int s, int hq,
@@ -335,7 +342,7 @@ __global__ void __launch_bounds__(64 * HPB, 1)
                     int *__restrict__ slot_start, uint16_t *__restrict__ out, float *__restrict__ lse,
                     uint16_t *__restrict__ part_out, float *__restrict__ part_lse)
 {
-    using C = GqaMfmaCfg<D, RBLK, HPB, NST>;
+    using C = GqaMfmaCfg<D, RBLK, HPB, NST, DV>;
     constexpr int SUB = kGqaTile / C::T;  // stages per planner tile
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     DA_LDS char *lds = (DA_LDS char *)smem;
@@ -363,17 +370,18 @@ __global__ void __launch_bounds__(64 * HPB, 1)
     const int grp = hq / hkv;
     const int R = grp * s;       // query rows of this KV head
     const int M = s * hq;        // query rows per sequence
-    const size_t tok_elems = (size_t)hkv * D;
+    const int tok_k = hkv * D;   // elements of one token's K row (all KV heads)
+    const int tok_v = hkv * DV;  // ... and V row
 
-    // ---- per-lane LDS offsets
-    const int qk_base = n * C::ROWB;  // + ((chunk ^ gsw(n)) << 4)
+    // ---- per-lane LDS offsets (stage: T K token rows, then T V token rows)
+    const int qk_base = n * C::ROWK;  // + ((chunk ^ gsw(n)) << 4)
     const int sq = gqa_swz(n);
     const int tr_tok = 4 * g + (n >> 2);
     const int st = gqa_swz(tr_tok);
     const int hsel = (n & 3) >> 1;
-    const int tr_base = (C::T + tr_tok) * C::ROWB + ((n & 1) << 3);
+    const int tr_base = C::T * C::ROWK + tr_tok * C::ROWV + ((n & 1) << 3);
 
-    // ---- DMA of one stage: 1 KB copies w, w + HPB, ... (token rows 0..15 K, 16..31 V)
+    // ---- DMA of one stage: 1 KB copies w, w + HPB, ... (the K rows' chunks, then the V rows')
     PlanWalk icur = cur;  // the copies' own cursor, ahead of the compute's
     auto stage_pos = [&](int sg, int &bq, int &tok0) {
         const int tt = tile_lo + sg / SUB;
@@ -381,23 +389,24 @@ __global__ void __launch_bounds__(64 * HPB, 1)
         bq = icur.b;
         tok0 = (tt - icur.ts) * kGqaTile + (sg % SUB) * C::T;
     };
-    const int lrow = lane / C::LPR;  // token row of this lane within a copy
-    const int lchk = lane % C::LPR;  // 16-byte chunk of this lane within its row
     auto issue_stage = [&](int sg) {
         int bq, tok0;
         stage_pos(sg, bq, tok0);
         const int L = clamp_len(seqlens[bq], t_max);
-        const int nrec = L * (int)tok_elems * 2;
         DA_LDS char *dst = lds + (sg % C::NST) * C::STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < C::LW; ++i) {
-            const int cp = w + i * C::HPB;           // wave-uniform copy index
-            const int r = cp * C::RPC + lrow;        // K rows 0..T-1, V rows T..2T-1
-            const int tk = r & (C::T - 1);
-            const uint16_t *base = (cp * C::RPC < C::T ? kc : vc) + (size_t)bq * t_max * tok_elems;
-            const u32x4 rsrc = raw_buffer_rsrc(base, (uint32_t)nrec);
-            const int c = lchk ^ gqa_swz(tk);
-            const uint32_t off = (uint32_t)(((tok0 + tk) * (int)tok_elems + hb * C::HPB * D) * 2 + c * 16);
+            const int cp = w + i * C::HPB;  // wave-uniform copy index
+            const int p = cp * 64 + lane;   // 16-byte chunk of the stage
+            const bool is_k = cp * 64 < C::KCH;
+            const int rch = is_k ? C::ROWK / 16 : C::ROWV / 16;  // chunks per token row
+            const int q = is_k ? p : p - C::KCH;
+            const int tk = q / rch;                             // token row of the stage
+            const int c = (q - tk * rch) ^ gqa_swz(tk);         // logical chunk in that row
+            const int te = is_k ? tok_k : tok_v;
+            const uint16_t *base = (is_k ? kc : vc) + (size_t)bq * t_max * te;
+            const u32x4 rsrc = raw_buffer_rsrc(base, (uint32_t)(L * te * 2));
+            const uint32_t off = (uint32_t)(((tok0 + tk) * te + hb * C::HPB * (is_k ? D : DV)) * 2 + c * 16);
             lds_dma16(rsrc, dst + cp * 1024, off);
         }
     };
@@ -449,8 +458,8 @@ __global__ void __launch_bounds__(64 * HPB, 1)
             const float inv = lsum[rb] > 0.f ? 1.f / lsum[rb] : 0.f;
             const float lse2 = lsum[rb] > 0.f ? mref[rb] + fast_log2(lsum[rb]) : -INFINITY;
             // the result, or this segment's bf16 partial for the combine
-            uint16_t *o = nseg == 1 ? out + ((size_t)bq * M + row) * D + g * 4
-                                    : part_out + ((size_t)sl * M + row) * D + g * 4;
+            uint16_t *o = nseg == 1 ? out + ((size_t)bq * M + row) * DV + g * 4
+                                    : part_out + ((size_t)sl * M + row) * DV + g * 4;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
                 u32x2 v;
@@ -539,7 +548,7 @@ __global__ void __launch_bounds__(64 * HPB, 1)
         // values
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-            const int c = w * (D / 8) + 2 * db + hsel;
+            const int c = w * (DV / 8) + 2 * db + hsel;
             const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (DA_LDS i16x4 *)(stg + tr_base + ((c ^ st) << 4)));
 #pragma unroll

@@ -130,6 +130,33 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
                      float scale, uint16_t *out, float *lse, void *workspace,
                      size_t workspace_bytes, int num_workers, int path, void *stream);
 
+/* Bytes of workspace mla_decode_unabsorbed needs (0 for arguments it would
+ * reject). */
+size_t mla_decode_unabsorbed_workspace_size(int b, int s, int h, int dqk, int dv, int t_max, int num_workers);
+
+/*
+ * Un-absorbed (FlashAttention-style) MLA decode: the same attention as
+ * mla_decode, computed on per-head decompressed keys and values instead of the
+ * shared latent ("MLA Cost Analysis & Regime Guide": "Cost Models",
+ * FlashAttention, whose byte count charges per head and token a d + p key row
+ * and a d value row; "Regime Selection" sets it against FlashMLA as s grows).
+ * Every query head has its own K/V head (hkv = h).
+ *   q       [b, s, h, dqk]      bf16   per head [q_nope | q_rope]
+ *   k_cache [b, t_max, h, dqk]  bf16   per token and head [k_nope | k_rope]
+ *   v_cache [b, t_max, h, dv]   bf16
+ *   seqlens [b]                 int32  valid cache rows, drafts included
+ *   scale                       fp32   multiplies q . k
+ *   out     [b, s, h, dv]       bf16
+ *   lse     [b, s, h]           fp32   natural log
+ * Draft mask, ownership, errors and workspace as for mla_decode.
+ * Compiled set: (dqk, dv) = (192, 128) (DeepSeek's 128 + 64 rope / 128);
+ * s <= 64; t_max * h * dqk * 2 < 2^31.
+ */
+da_status mla_decode_unabsorbed(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                                const int32_t *seqlens, int b, int s, int h, int dqk, int dv, int t_max,
+                                float scale, uint16_t *out, float *lse, void *workspace,
+                                size_t workspace_bytes, int num_workers, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,13 +34,16 @@ def lib():
     L.gqa_decode_workspace_size.argtypes, L.gqa_decode_workspace_size.restype = [I] * 8, Z
     L.mla_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, P]
     L.gqa_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, I, P]
+    L.mla_decode_unabsorbed_workspace_size.argtypes = [I] * 7
+    L.mla_decode_unabsorbed_workspace_size.restype = Z
+    L.mla_decode_unabsorbed.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, P]
     return L
 
 
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     for n in ("mla_decode", "gqa_decode", "mla_decode_workspace_size", "gqa_decode_workspace_size",
-              "da_status_string", "da_version"):
+              "mla_decode_unabsorbed", "mla_decode_unabsorbed_workspace_size", "da_status_string", "da_version"):
         assert n in names
 
 
@@ -124,3 +127,28 @@ def test_workspace_size_explicit_workers(lib):
     assert sz < slots * s * h * (2 * k + 4) + 64 * 1024
     # too-small workspace is reported as such (checked before any launch)
     assert mla_call(lib, b=b, s=s, h=h, t=t, nw=w, wsb=sz - 1, ws=ctypes.c_void_p(0x100000)) == DA_ERR_WORKSPACE
+
+
+def unabs_call(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sl=FAKE, b=2, s=1, h=16, dqk=192, dv=128, t=128, scale=0.1, o=FAKE, lse=FAKE,
+             ws=FAKE, wsb=0, nw=0)
+    a.update(kw)
+    return lib.mla_decode_unabsorbed(a["q"], a["k"], a["v"], a["sl"], a["b"], a["s"], a["h"], a["dqk"], a["dv"],
+                                     a["t"], a["scale"], a["o"], a["lse"], a["ws"], a["wsb"], a["nw"], None)
+
+
+@pytest.mark.parametrize("kw, code", [
+    ({"dqk": 128}, 2), ({"dv": 192}, 2), ({"b": 0}, 1), ({"h": -1}, 1), ({"s": 65}, 2), ({"s": 200}, 1),
+    ({"nw": -2}, 1), ({"t": 100000, "h": 128}, 2), ({"scale": float("nan")}, 1), ({"scale": 0.0}, 1),
+    ({"q": None}, 1), ({"v": None}, 1), ({"o": ctypes.c_void_p(0x100008)}, 1), ({}, 3),
+])
+def test_unabsorbed_rejects(lib, kw, code):
+    assert unabs_call(lib, **kw) == code
+
+
+def test_unabsorbed_workspace_size(lib):
+    assert lib.mla_decode_unabsorbed_workspace_size(2, 1, 16, 128, 128, 128, 0) == 0
+    b, s, h, w = 4, 2, 8, 10
+    sz = lib.mla_decode_unabsorbed_workspace_size(b, s, h, 192, 128, 512, w)
+    # per partial slot and query row: 128 bf16 outputs and one fp32 lse
+    assert (b + w) * s * h * (2 * 128 + 4) <= sz < (b + w) * s * h * (2 * 128 + 4) + 64 * 1024

@@ -352,6 +352,89 @@ def test_gqa_many_segments_per_row(da, oracle_mod, case, path):
     compare(out, lse, ref_o, ref_l, "gqa many segments %s path %d" % (case, path))
 
 
+# ------------------------------------------------------------------ un-absorbed MLA (per-head K and V)
+def unabsorbed_inputs(b, s, h, t, seqlens, seed):
+    gen = torch.Generator().manual_seed(seed)
+    q = torch.randn((b, s, h, 192), generator=gen).to(torch.bfloat16)
+    k = torch.randn((b, t, h, 192), generator=gen).to(torch.bfloat16)
+    v = torch.randn((b, t, h, 128), generator=gen).to(torch.bfloat16)
+    return q, k, v, torch.tensor(seqlens, dtype=torch.int32)
+
+
+def unabsorbed_reference(oracle_mod, q, k, v, sl, scale):
+    """Per sequence and head: textbook attention of the s drafts over the
+    visible cache rows (draft i sees L - s + i + 1 of them)."""
+    b, s, h, _ = q.shape
+    out = np.zeros((b, s, h, 128))
+    lse = np.full((b, s, h), -np.inf)
+    for bq in range(b):
+        L = max(0, min(int(sl[bq]), k.shape[1]))
+        n_vis = [max(0, L - s + i + 1) for i in range(s)]
+        if L == 0:
+            continue
+        for hh in range(h):
+            o, l = oracle_mod.attn_generic(q[bq, :, hh].double().numpy(), k[bq, :L, hh].double().numpy(),
+                                           v[bq, :L, hh].double().numpy(), n_vis, scale)
+            out[bq, :, hh], lse[bq, :, hh] = o, l
+    return out, lse
+
+
+UNABS_SMALL = [
+    # (b, s, h, t_max, seqlens, workers)
+    (2, 1, 4, 150, [150, 77], 0),
+    (3, 3, 8, 100, [100, 2, 0], 0),       # drafts, L < s, an empty sequence
+    (1, 16, 4, 200, [200], 3),            # 16 drafts: one 16-row block
+    (2, 20, 2, 130, [130, 64], 2),        # 20 drafts: two row blocks
+    (1, 40, 2, 300, [300], 5),            # 40 drafts: four row blocks
+    (2, 1, 5, 1000, [1000, 999], 0),      # odd head count: the last head block has one active wave
+    (2, 2, 3, 700, [700, 350], 40),       # many segments per row (block-per-row combine)
+]
+
+
+@pytest.mark.parametrize("case", UNABS_SMALL, ids=lambda c: "b%d_s%d_h%d_t%d_w%d" % (c[0], c[1], c[2], c[3], c[5]))
+def test_mla_unabsorbed_small(da, oracle_mod, case):
+    b, s, h, t, sl, workers = case
+    q, k, v, slt = unabsorbed_inputs(b, s, h, t, sl, seed=400 + b + s + h)
+    scale = 1.0 / math.sqrt(192)
+    d = dev()
+    out, lse = da.mla_decode_unabsorbed(q.to(d), k.to(d), v.to(d), slt.to(d), scale, num_workers=workers)
+    torch.cuda.synchronize()
+    ref_o, ref_l = unabsorbed_reference(oracle_mod, q, k, v, sl, scale)
+    compare(out.cpu(), lse.cpu(), ref_o, ref_l, "mla unabsorbed %s" % (case,))
+
+
+def test_mla_unabsorbed_matches_absorbed(da):
+    """With K = [Z Wk_h | Z_rope], V = Z Wv_h from a latent cache Z and
+    per-head weights, and q_lat = q_nope Wk_h^T: the un-absorbed output equals
+    the absorbed latent output times Wv_h^T (GPU against GPU, up to the bf16
+    rounding of the decompressed K/V, the absorbed queries and the latent
+    output)."""
+    b, s, h, t, kl, dn, p = 2, 2, 4, 200, 128, 128, 64
+    gen = torch.Generator().manual_seed(77)
+    Z = torch.randn((b, t, kl + p), generator=gen)
+    Wk = torch.randn((h, dn, kl), generator=gen) / math.sqrt(kl)
+    Wv = torch.randn((h, dn, kl), generator=gen) / math.sqrt(kl)
+    qn = torch.randn((b, s, h, dn), generator=gen)
+    qr = torch.randn((b, s, h, p), generator=gen)
+    sl = torch.tensor([200, 123], dtype=torch.int32)
+    scale = 1.0 / math.sqrt(dn + p)
+    Zb = Z.to(torch.bfloat16).float()
+    K = torch.cat([torch.einsum("btk,hdk->bthd", Zb[..., :kl], Wk), Zb[..., kl:].unsqueeze(2).expand(b, t, h, p)], -1)
+    V = torch.einsum("btk,hdk->bthd", Zb[..., :kl], Wv)
+    q = torch.cat([qn, qr], -1)
+    q_lat = torch.einsum("bshd,hdk->bshk", qn.to(torch.bfloat16).float(), Wk)
+    d = dev()
+    g16 = lambda x: x.to(torch.bfloat16).contiguous().to(d)  # noqa: E731
+    o_u, l_u = da.mla_decode_unabsorbed(g16(q), g16(K), g16(V), sl.to(d), scale)
+    o_a, l_a = da.mla_decode(g16(q_lat), g16(qr), g16(Z), sl.to(d), scale)
+    torch.cuda.synchronize()
+    o_a_dec = torch.einsum("bshk,hdk->bshd", o_a.float().cpu(), Wv)
+    o_u = o_u.float().cpu()
+    ref_max = o_a_dec.abs().max().item()
+    assert (o_u - o_a_dec).abs().max().item() <= 5e-2 * ref_max
+    assert (l_u.cpu() - l_a.cpu()).abs().max().item() <= 3e-2
+
+
 @pytest.fixture(scope="module")
 def gqa_long_case(oracle_mod):
     """One 262,144-token sequence at 24 query / 4 KV heads, d = 256, with the
