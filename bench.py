@@ -123,6 +123,55 @@ class UnabsorbedPart:
         binding.mla_decode_unabsorbed(self.q, k, v, sl, self.scale, out=self.out, lse=self.lse, workspace=self.ws)
 
 
+class ProjectionPart:
+    """One per-head projection call at the DeepSeek-V3-like shapes (h=128, d=128, k=512): the query
+    absorption or the output decompression for b*s query tokens."""
+
+    def __init__(self, kind, s, dev, b=32, h=128, d=128, k=512):
+        self.name, self.kind = "%s_s%d" % (kind, s), kind
+        g = torch.Generator(device=dev).manual_seed(11 + s)
+        if kind == "absorb":
+            self.a = torch.randn((b, s, h, d), generator=g, device=dev, dtype=torch.bfloat16)
+            self.w = torch.randn((h, k, d), generator=g, device=dev, dtype=torch.bfloat16)
+            self.out = torch.empty((b, s, h, k), dtype=torch.bfloat16, device=dev)
+        else:
+            self.a = torch.randn((b, s, h, k), generator=g, device=dev, dtype=torch.bfloat16)
+            self.w = torch.randn((h, d, k), generator=g, device=dev, dtype=torch.bfloat16)
+            self.out = torch.empty((b, s, h, d), dtype=torch.bfloat16, device=dev)
+        m = b * s
+        self.flops = 2.0 * m * h * d * k
+        self.bytes = 2.0 * (h * d * k + m * h * d + m * h * k)  # weights once, input and output rows
+
+    def __call__(self):
+        if self.kind == "absorb":
+            binding.mla_absorb_queries(self.a, self.w, out=self.out)
+        else:
+            binding.mla_decompress_output(self.a, self.w, out=self.out)
+
+
+class SplitPart:
+    """One split-cache MLA decode call (b=32, h=128, t=4096 = o latent + n decompressed rows, s drafts),
+    inputs drawn on the GPU from a seeded generator."""
+
+    def __init__(self, s, n, dev, b=32, h=128, t=4096):
+        self.name, self.s, self.n = "split_s%d_n%d" % (s, n), s, n
+        o = t - n
+        g = torch.Generator(device=dev).manual_seed(900 + n)
+        r = lambda *shape: torch.randn(shape, generator=g, device=dev, dtype=torch.bfloat16)  # noqa: E731
+        self.args = (r(b, s, h, 128), r(b, s, h, 64), r(h, 512, 128), r(h, 128, 512), r(b, max(o, 1), 576),
+                     torch.full((b,), o, dtype=torch.int32, device=dev), r(b, n, h, 192), r(b, n, h, 128),
+                     torch.full((b,), n, dtype=torch.int32, device=dev))
+        self.scale = 1.0 / math.sqrt(192)
+        self.out = torch.empty((b, s, h, 128), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
+        nbytes = binding.mla_decode_split_cache_workspace_size(b, s, h, max(o, 1), n, 0)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.cost = cm.mla_split_latent(b, h, s, o, n, 128, 512, 64)
+
+    def __call__(self):
+        binding.mla_decode_split_cache(*self.args, self.scale, out=self.out, lse=self.lse, workspace=self.ws)
+
+
 def time_parts(parts, steps, warmup):
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -189,6 +238,10 @@ def main():
     ap.add_argument("--ragged", action="store_true", help="only the ragged long-context MLA workload")
     ap.add_argument("--crossover", action="store_true",
                     help="absorbed vs un-absorbed MLA decode over the s-sweep (b=32, h=128, t=4096)")
+    ap.add_argument("--split", action="store_true",
+                    help="split latent/decompressed cache at s=16 over n (b=32, h=128, t=4096)")
+    ap.add_argument("--projections", action="store_true",
+                    help="per-head query absorption and output decompression (b=32, h=128, d=128, k=512)")
     ap.add_argument("--gqa-long", action="store_true",
                     help="only the long-context GQA workload (t=262144, hq=24, hkv=4, d=256), both kernels")
     ap.add_argument("--only", default="", help="comma list of parts to run (gqa,mla_s1,mla_s4)")
@@ -249,6 +302,41 @@ def main():
             del pa, pu
         print(json.dumps({"crossover_s": first, "note": "smallest s of the sweep at which the un-absorbed kernel "
                           "is faster (null: none up to s=64)"}), flush=True)
+        return
+
+    if args.split:
+        s = 16
+        pa = Part("absorbed_s%d" % s, "mla", wl.mla_mtp(s), dev)
+        _, per = time_parts([pa], args.steps, args.warmup)
+        print(json.dumps({"split": "absorbed only (n=0)", "s": s, "us": round(per[pa.name] * 1e6, 2)}), flush=True)
+        del pa
+        for n in (64, 256, 1024, 2048, 4096):
+            p = SplitPart(s, n, dev)
+            _, per = time_parts([p], args.steps, args.warmup)
+            sec = per[p.name]
+            t_min = cm.roofline_time(p.cost)
+            print(json.dumps({"split": "latent o + decompressed n (b=32, h=128, t=4096)", "s": s, "o": 4096 - n,
+                              "n": n, "us": round(sec * 1e6, 2), "tflops": round(p.cost.flops / sec / 1e12, 2),
+                              "tbs": round(p.cost.bytes / sec / 1e12, 3), "ai": round(p.cost.ai, 1),
+                              "t_min_us": round(t_min * 1e6, 2), "roofline_frac": round(t_min / sec, 4)}),
+                  flush=True)
+            del p
+            torch.cuda.empty_cache()
+        return
+
+    if args.projections:
+        for s in (1, 4, 32):
+            for kind in ("absorb", "decompress"):
+                p = ProjectionPart(kind, s, dev)
+                _, per = time_parts([p], args.steps, args.warmup)
+                sec = per[p.name]
+                t_min = max(p.flops / cm.MI355X_BF16_FLOPS, p.bytes / cm.MI355X_HBM_BYTES_PER_S)
+                print(json.dumps({"projection": kind, "b": 32, "s": s, "h": 128, "d": 128, "k": 512,
+                                  "us": round(sec * 1e6, 2), "tflops": round(p.flops / sec / 1e12, 2),
+                                  "tbs": round(p.bytes / sec / 1e12, 3), "ai": round(p.flops / p.bytes, 1),
+                                  "t_min_us": round(t_min * 1e6, 2), "roofline_frac": round(t_min / sec, 4)}),
+                      flush=True)
+                del p
         return
 
     if args.gqa_long:

@@ -24,7 +24,8 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dimensions", 3: "work
 
 EXPORTED = ("da_version", "da_status_string", "mla_decode_workspace_size", "mla_decode",
             "gqa_decode_workspace_size", "gqa_decode", "mla_decode_unabsorbed_workspace_size",
-            "mla_decode_unabsorbed")
+            "mla_decode_unabsorbed", "mla_absorb_queries", "mla_decompress_output",
+            "mla_decode_split_cache_workspace_size", "mla_decode_split_cache")
 
 
 class DecodeAttentionError(RuntimeError):
@@ -63,6 +64,14 @@ def load_library():
         lib.mla_decode_unabsorbed_workspace_size.restype = Z
         lib.mla_decode_unabsorbed.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, P]
         lib.mla_decode_unabsorbed.restype = I
+        lib.mla_absorb_queries.argtypes = [P, P, P, I, I, I, I, I, P]
+        lib.mla_absorb_queries.restype = I
+        lib.mla_decompress_output.argtypes = [P, P, P, I, I, I, I, I, P]
+        lib.mla_decompress_output.restype = I
+        lib.mla_decode_split_cache_workspace_size.argtypes = [I] * 6
+        lib.mla_decode_split_cache_workspace_size.restype = Z
+        lib.mla_decode_split_cache.argtypes = [P] * 9 + [I] * 5 + [F, P, P, P, Z, I, P]
+        lib.mla_decode_split_cache.restype = I
         _lib = lib
         return lib
 
@@ -106,6 +115,10 @@ def gqa_decode_workspace_size(b, s, hq, hkv, d, t_max, num_workers=0, path=0) ->
 
 def mla_decode_unabsorbed_workspace_size(b, s, h, dqk, dv, t_max, num_workers=0) -> int:
     return int(load_library().mla_decode_unabsorbed_workspace_size(b, s, h, dqk, dv, t_max, num_workers))
+
+
+def mla_decode_split_cache_workspace_size(b, s, h, o_max, n_max, num_workers=0) -> int:
+    return int(load_library().mla_decode_split_cache_workspace_size(b, s, h, o_max, n_max, num_workers))
 
 
 def _workspace(nbytes, device, workspace):
@@ -225,4 +238,82 @@ def mla_decode_unabsorbed(q, k_cache, v_cache, seqlens, scale, num_workers=0, ou
                                        float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                        int(num_workers), _stream(dev))
     _check("mla_decode_unabsorbed", rc)
+    return out, lse
+
+
+def mla_absorb_queries(q_nope, w_k, out=None):
+    """q_lat [b,s,h,k] = per head w_k[h] . q_nope[b,s,h,:]; q_nope [b,s,h,d], w_k [h,k,d] (bf16)."""
+    lib = load_library()
+    _need(q_nope, "q_nope", torch.bfloat16, 4)
+    dev = q_nope.device
+    _need(w_k, "w_k", torch.bfloat16, 3, dev)
+    b, s, h, d = q_nope.shape
+    if w_k.shape[0] != h or w_k.shape[2] != d:
+        raise ValueError("w_k must be [h, k, d] = [%d, k, %d]" % (h, d))
+    k = w_k.shape[1]
+    if out is None:
+        out = torch.empty((b, s, h, k), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, 4, dev)
+    with torch.cuda.device(dev):
+        rc = lib.mla_absorb_queries(_ptr(q_nope), _ptr(w_k), _ptr(out), b, s, h, d, k, _stream(dev))
+    _check("mla_absorb_queries", rc)
+    return out
+
+
+def mla_decompress_output(o_lat, w_v_t, out=None):
+    """out [b,s,h,d] = per head w_v_t[h] . o_lat[b,s,h,:]; o_lat [b,s,h,k], w_v_t [h,d,k] (bf16)."""
+    lib = load_library()
+    _need(o_lat, "o_lat", torch.bfloat16, 4)
+    dev = o_lat.device
+    _need(w_v_t, "w_v_t", torch.bfloat16, 3, dev)
+    b, s, h, k = o_lat.shape
+    if w_v_t.shape[0] != h or w_v_t.shape[2] != k:
+        raise ValueError("w_v_t must be [h, d, k] = [%d, d, %d]" % (h, k))
+    d = w_v_t.shape[1]
+    if out is None:
+        out = torch.empty((b, s, h, d), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, 4, dev)
+    with torch.cuda.device(dev):
+        rc = lib.mla_decompress_output(_ptr(o_lat), _ptr(w_v_t), _ptr(out), b, s, h, k, d, _stream(dev))
+    _check("mla_decompress_output", rc)
+    return out
+
+
+def mla_decode_split_cache(q_nope, q_rope, w_k, w_v_t, latent, seqlens_old, k_new, v_new, seqlens_new, scale,
+                           num_workers=0, out=None, lse=None, workspace=None):
+    """MLA decode over a split cache: latent old rows plus decompressed new rows (see the C header).
+
+    q_nope [b,s,h,128], q_rope [b,s,h,64], w_k [h,512,128], w_v_t [h,128,512], latent [b,o_max,576],
+    k_new [b,n_max,h,192], v_new [b,n_max,h,128] (bf16); seqlens_old, seqlens_new [b] (int32).
+    Returns (out [b,s,h,128] bf16, lse [b,s,h] fp32).
+    """
+    lib = load_library()
+    _need(q_nope, "q_nope", torch.bfloat16, 4)
+    dev = q_nope.device
+    for t, nm, nd in ((q_rope, "q_rope", 4), (w_k, "w_k", 3), (w_v_t, "w_v_t", 3), (latent, "latent", 3),
+                      (k_new, "k_new", 4), (v_new, "v_new", 4)):
+        _need(t, nm, torch.bfloat16, nd, dev)
+    _need(seqlens_old, "seqlens_old", torch.int32, 1, dev)
+    _need(seqlens_new, "seqlens_new", torch.int32, 1, dev)
+    b, s, h, _ = q_nope.shape
+    o_max, n_max = latent.shape[1], k_new.shape[1]
+    if (tuple(q_nope.shape) != (b, s, h, 128) or tuple(q_rope.shape) != (b, s, h, 64)
+            or tuple(w_k.shape) != (h, 512, 128) or tuple(w_v_t.shape) != (h, 128, 512)
+            or tuple(latent.shape) != (b, o_max, 576) or tuple(k_new.shape) != (b, n_max, h, 192)
+            or tuple(v_new.shape) != (b, n_max, h, 128)):
+        raise ValueError("split-cache shapes: see mla_decode_split_cache in include/decode_attn.h")
+    if out is None:
+        out = torch.empty((b, s, h, 128), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
+    nbytes = lib.mla_decode_split_cache_workspace_size(b, s, h, o_max, n_max, num_workers)
+    ws = _workspace(nbytes, dev, workspace)
+    with torch.cuda.device(dev):
+        rc = lib.mla_decode_split_cache(_ptr(q_nope), _ptr(q_rope), _ptr(w_k), _ptr(w_v_t), _ptr(latent),
+                                        _ptr(seqlens_old), _ptr(k_new), _ptr(v_new), _ptr(seqlens_new), b, s, h,
+                                        o_max, n_max, float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                        ws.numel() * ws.element_size(), int(num_workers), _stream(dev))
+    _check("mla_decode_split_cache", rc)
     return out, lse

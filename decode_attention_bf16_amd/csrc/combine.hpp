@@ -195,6 +195,62 @@ __global__ void __launch_bounds__(64 * kCombineWideWaves) combine_wide_kernel(
     }
 }
 
+// Merge of two attention results over disjoint sets of cache rows (natural-log
+// lse): lse = log(e^l1 + e^l2), out = (e^l1 o1 + e^l2 o2) / (e^l1 + e^l2); a
+// side with lse = -inf weighs nothing, and both -inf give out = 0, lse = -inf.
+// One wave per row (grid-stride), DV columns over the 64 lanes.
+template <int DV>
+__global__ void __launch_bounds__(256) merge2_kernel(long rows, const uint16_t *__restrict__ o1,
+                                                     const float *__restrict__ l1, const uint16_t *__restrict__ o2,
+                                                     const float *__restrict__ l2, uint16_t *__restrict__ out,
+                                                     float *__restrict__ lse)
+{
+    constexpr int CPL = DV / 64;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    for (long row = (long)blockIdx.x * 4 + wave; row < rows; row += (long)gridDim.x * 4) {
+        const float a = l1[row], b = l2[row];
+        const float m = fmaxf(a, b);
+        float acc[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+        float wsum = 0.f;
+        if (m != -INFINITY) {
+            const float wa = fast_exp2((a - m) * kLog2e), wb = fast_exp2((b - m) * kLog2e);
+            float o[CPL];
+            if (wa > 0.f) {  // a side that weighs nothing is not read
+                load_partial<CPL>(o1 + (size_t)row * DV + lane * CPL, o);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) acc[c] += wa * o[c];
+            }
+            if (wb > 0.f) {
+                load_partial<CPL>(o2 + (size_t)row * DV + lane * CPL, o);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) acc[c] += wb * o[c];
+            }
+            wsum = wa + wb;
+        }
+        // combine_write takes the maximum in log2 units
+        combine_write<DV>(out, lse, row, lane, acc, wsum, m * kLog2e);
+    }
+}
+
+// out[row] = [a[row] | b[row]] for rows of wa and wb bf16 values (both
+// multiples of 8): 16-byte chunks, one per thread (grid-stride).
+__global__ void __launch_bounds__(256) concat_rows_kernel(const uint16_t *__restrict__ a, int wa,
+                                                          const uint16_t *__restrict__ b, int wb,
+                                                          uint16_t *__restrict__ out, long rows)
+{
+    const int ca = wa / 8, cb = wb / 8, cr = ca + cb;
+    const long total = rows * cr;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
+        const long row = i / cr;
+        const int c = (int)(i - row * cr);
+        const u32x4 v = c < ca ? *(const u32x4 *)(a + row * wa + 8 * c) : *(const u32x4 *)(b + row * wb + 8 * (c - ca));
+        *(u32x4 *)(out + row * (wa + wb) + 8 * c) = v;
+    }
+}
+
 // Blocks of the one-wave-per-row launch: enough to cover the rows with a few
 // waves per CU, never more than one block per four rows.
 inline unsigned combine_grid(long rows, int cus)

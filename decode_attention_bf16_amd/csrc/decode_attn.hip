@@ -2,6 +2,7 @@
 // choice and kernel launches. See include/decode_attn.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -10,6 +11,7 @@
 
 #include "../../include/decode_attn.h"
 #include "combine.hpp"
+#include "head_gemm.hpp"
 #include "common.hpp"
 #include "gqa_kernel.hpp"
 #include "mla_kernel.hpp"
@@ -510,6 +512,125 @@ da_status mla_decode_unabsorbed(const uint16_t *q, const uint16_t *k_cache, cons
                             part_out, part_lse, workers, st_);
     if (e != hipSuccess) return DA_ERR_HIP;
     launch_combine<kUnabsDV>(b, s * h, workers, hdr, slot_start, part_out, part_lse, out, lse, st_);
+    return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ per-head projections
+static da_status head_gemm(const uint16_t *a, const uint16_t *bw, uint16_t *c, int m, int h, int n, int k,
+                           void *stream)
+{
+    if (!a || !bw || !c || m <= 0 || h <= 0 || n <= 0 || k <= 0) return DA_ERR_INVALID_ARG;
+    if (k % 32 != 0 || (n + da::kGemmTile - 1) / da::kGemmTile > 65535 ||
+        (m + da::kGemmTile - 1) / da::kGemmTile > 65535)
+        return DA_ERR_UNSUPPORTED;
+    if (!aligned16(a) || !aligned16(bw) || !aligned16(c)) return DA_ERR_INVALID_ARG;
+    const dim3 grid(h, (n + da::kGemmTile - 1) / da::kGemmTile, (m + da::kGemmTile - 1) / da::kGemmTile);
+    hipLaunchKernelGGL(da::head_gemm_kernel, grid, dim3(256), 0, (hipStream_t)stream, a, bw, c, m, h, n, k);
+    return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+da_status mla_absorb_queries(const uint16_t *q_nope, const uint16_t *w_k, uint16_t *q_lat, int b, int s, int h,
+                             int d, int k, void *stream)
+{
+    if (b <= 0 || s <= 0) return DA_ERR_INVALID_ARG;
+    return head_gemm(q_nope, w_k, q_lat, b * s, h, k, d, stream);
+}
+
+da_status mla_decompress_output(const uint16_t *o_lat, const uint16_t *w_v_t, uint16_t *out, int b, int s, int h,
+                                int k, int d, void *stream)
+{
+    if (b <= 0 || s <= 0) return DA_ERR_INVALID_ARG;
+    return head_gemm(o_lat, w_v_t, out, b * s, h, d, k, stream);
+}
+
+// ------------------------------------------------------------------ split latent / decompressed cache
+// Workspace of mla_decode_split_cache: the intermediates, then the inner calls'
+// own workspaces.
+struct SplitWs {
+    size_t q_lat, q_full, o_lat, lse_old, out_old, out_new, lse_new, ws_abs, ws_unabs, total;
+    size_t ws_abs_bytes, ws_unabs_bytes;
+};
+static SplitWs split_ws(int b, int s, int h, int o_max, int n_max, int num_workers)
+{
+    SplitWs w{};
+    const size_t rows = (size_t)b * s * h;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = da::align256(off + bytes);
+        return at;
+    };
+    w.q_lat = take(rows * 512 * 2);
+    w.q_full = take(rows * 192 * 2);
+    w.o_lat = take(rows * 512 * 2);
+    w.lse_old = take(rows * 4);
+    w.out_old = take(rows * 128 * 2);
+    w.out_new = take(rows * 128 * 2);
+    w.lse_new = take(rows * 4);
+    w.ws_abs_bytes = mla_decode_workspace_size(b, 1, s * h, 512, 64, o_max, num_workers);
+    w.ws_unabs_bytes = mla_decode_unabsorbed_workspace_size(b, s, h, 192, 128, n_max, num_workers);
+    w.ws_abs = take(w.ws_abs_bytes);
+    w.ws_unabs = take(w.ws_unabs_bytes);
+    w.total = off;
+    return w;
+}
+
+static da_status split_check(int b, int s, int h, int o_max, int n_max, int num_workers)
+{
+    if (b <= 0 || s <= 0 || h <= 0 || o_max <= 0 || n_max <= 0 || num_workers < 0) return DA_ERR_INVALID_ARG;
+    if (s > n_max) return DA_ERR_INVALID_ARG;
+    if (mla_decode_workspace_size(b, 1, s * h, 512, 64, o_max, num_workers) == 0) return DA_ERR_UNSUPPORTED;
+    if (mla_decode_unabsorbed_workspace_size(b, s, h, 192, 128, n_max, num_workers) == 0) return DA_ERR_UNSUPPORTED;
+    return DA_OK;
+}
+
+size_t mla_decode_split_cache_workspace_size(int b, int s, int h, int o_max, int n_max, int num_workers)
+{
+    if (split_check(b, s, h, o_max, n_max, num_workers) != DA_OK) return 0;
+    return split_ws(b, s, h, o_max, n_max, num_workers).total;
+}
+
+da_status mla_decode_split_cache(const uint16_t *q_nope, const uint16_t *q_rope, const uint16_t *w_k,
+                                 const uint16_t *w_v_t, const uint16_t *latent, const int32_t *seqlens_old,
+                                 const uint16_t *k_new, const uint16_t *v_new, const int32_t *seqlens_new, int b,
+                                 int s, int h, int o_max, int n_max, float scale, uint16_t *out, float *lse,
+                                 void *workspace, size_t workspace_bytes, int num_workers, void *stream)
+{
+    da_status st = split_check(b, s, h, o_max, n_max, num_workers);
+    if (st != DA_OK) return st;
+    if (!q_nope || !q_rope || !w_k || !w_v_t || !latent || !seqlens_old || !k_new || !v_new || !seqlens_new || !out ||
+        !lse || !workspace)
+        return DA_ERR_INVALID_ARG;
+    if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(out) || ((uintptr_t)workspace & 255u) != 0)
+        return DA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return DA_ERR_INVALID_ARG;
+    const SplitWs w = split_ws(b, s, h, o_max, n_max, num_workers);
+    if (workspace_bytes < w.total) return DA_ERR_WORKSPACE;
+    char *wsp = (char *)workspace;
+    auto *q_lat = (uint16_t *)(wsp + w.q_lat);
+    auto *q_full = (uint16_t *)(wsp + w.q_full);
+    auto *o_lat = (uint16_t *)(wsp + w.o_lat);
+    auto *lse_old = (float *)(wsp + w.lse_old);
+    auto *out_old = (uint16_t *)(wsp + w.out_old);
+    auto *out_new = (uint16_t *)(wsp + w.out_new);
+    auto *lse_new = (float *)(wsp + w.lse_new);
+    const long rows = (long)b * s * h;
+    hipStream_t st_ = (hipStream_t)stream;
+    // old rows, latent and absorbed: every draft sees all of them, so the s
+    // drafts of a sequence are s*h independent query rows of one step
+    if ((st = mla_absorb_queries(q_nope, w_k, q_lat, b, s, h, 128, 512, stream)) != DA_OK) return st;
+    if ((st = mla_decode(q_lat, q_rope, latent, seqlens_old, b, 1, s * h, 512, 64, o_max, scale, o_lat, lse_old,
+                         wsp + w.ws_abs, w.ws_abs_bytes, num_workers, stream)) != DA_OK)
+        return st;
+    if ((st = mla_decompress_output(o_lat, w_v_t, out_old, b, s, h, 512, 128, stream)) != DA_OK) return st;
+    // new rows, decompressed: the drafts' causal mask applies here
+    const unsigned cgrid = (unsigned)std::min<long>((rows * 24 + 255) / 256, 4L * current_cu_count());
+    hipLaunchKernelGGL(da::concat_rows_kernel, dim3(cgrid), dim3(256), 0, st_, q_nope, 128, q_rope, 64, q_full, rows);
+    if ((st = mla_decode_unabsorbed(q_full, k_new, v_new, seqlens_new, b, s, h, 192, 128, n_max, scale, out_new,
+                                    lse_new, wsp + w.ws_unabs, w.ws_unabs_bytes, num_workers, stream)) != DA_OK)
+        return st;
+    hipLaunchKernelGGL(da::merge2_kernel<128>, dim3(da::combine_grid(rows, current_cu_count())), dim3(256), 0, st_,
+                       rows, out_old, lse_old, out_new, lse_new, out, lse);
     return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

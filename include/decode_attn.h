@@ -157,6 +157,54 @@ da_status mla_decode_unabsorbed(const uint16_t *q, const uint16_t *k_cache, cons
                                 float scale, uint16_t *out, float *lse, void *workspace,
                                 size_t workspace_bytes, int num_workers, void *stream);
 
+/*
+ * Per-head projections either side of absorbed MLA decode ("MLA Cost Analysis
+ * & Regime Guide", "Absorption Trick (FlashMLA)": the queries enter latent
+ * space through Wk^T before the attention; a separate kernel decompresses the
+ * latent output with Wv after it). For every head hd:
+ *   mla_absorb_queries:    q_lat[b,s,hd,:] = w_k[hd] . q_nope[b,s,hd,:]
+ *       q_nope [b,s,h,d], w_k [h,k,d] (Wk of the head: latent row c holds a d-vector), q_lat [b,s,h,k]
+ *   mla_decompress_output: out[b,s,hd,:] = w_v_t[hd] . o_lat[b,s,hd,:]
+ *       o_lat [b,s,h,k], w_v_t [h,d,k] (Wv of the head transposed: row j holds a k-vector), out [b,s,h,d]
+ * bf16 in and out (round to nearest even), fp32 accumulation. The contracted
+ * width (d for the queries, k for the output) must be a multiple of 32 and all
+ * three tensors 16-byte aligned. No workspace; queued asynchronously on `stream`.
+ * Errors: DA_ERR_INVALID_ARG (null pointer, dimension <= 0, misaligned input),
+ * DA_ERR_UNSUPPORTED (contracted width not a multiple of 32, more than 65535
+ * tiles of 64 output columns or of 64 query tokens).
+ */
+da_status mla_absorb_queries(const uint16_t *q_nope, const uint16_t *w_k, uint16_t *q_lat, int b, int s, int h,
+                             int d, int k, void *stream);
+da_status mla_decompress_output(const uint16_t *o_lat, const uint16_t *w_v_t, uint16_t *out, int b, int s, int h,
+                                int k, int d, void *stream);
+
+/* Bytes of workspace mla_decode_split_cache needs (0 for arguments it would reject). */
+size_t mla_decode_split_cache_workspace_size(int b, int s, int h, int o_max, int n_max, int num_workers);
+
+/*
+ * MLA decode over a split cache ("MLA Cost Analysis & Regime Guide", "MLAvar6+
+ * Design"): the o older tokens of a sequence stay as latent rows, the n newest
+ * (the s drafts among them) are kept decompressed per head. Attention over all
+ * o + n tokens, computed as absorbed attention on the old part (queries taken
+ * into latent space with w_k, output decompressed with w_v_t), un-absorbed
+ * attention on the new part, and a log-sum-exp merge of the two.
+ *   q_nope  [b,s,h,128], q_rope [b,s,h,64]   bf16
+ *   w_k     [h,512,128], w_v_t [h,128,512]    bf16 (as for the projections above)
+ *   latent  [b,o_max,576]  bf16, seqlens_old [b] int32 (o per sequence, clamped)
+ *   k_new   [b,n_max,h,192], v_new [b,n_max,h,128]  bf16, seqlens_new [b] int32
+ *   out     [b,s,h,128] bf16, lse [b,s,h] fp32 (natural log)
+ * Draft i sees every old row and the first n - s + i + 1 new rows (the drafts'
+ * own rows are the last s of the new part, so n >= s; with n < s the drafts'
+ * order across the split is not the un-split one). Compiled set: latent 512,
+ * rope 64, head 128; s <= n_max, s <= 64. Workspace, ownership and errors as
+ * for mla_decode.
+ */
+da_status mla_decode_split_cache(const uint16_t *q_nope, const uint16_t *q_rope, const uint16_t *w_k,
+                                 const uint16_t *w_v_t, const uint16_t *latent, const int32_t *seqlens_old,
+                                 const uint16_t *k_new, const uint16_t *v_new, const int32_t *seqlens_new, int b,
+                                 int s, int h, int o_max, int n_max, float scale, uint16_t *out, float *lse,
+                                 void *workspace, size_t workspace_bytes, int num_workers, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

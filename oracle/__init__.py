@@ -175,3 +175,32 @@ def attn_generic(Q, K, V, n_vis, scale):
     if rc != 0:
         raise ValueError("oracle_attn_generic rejected its arguments")
     return out, lse
+
+
+def _wide(a) -> np.ndarray:
+    """bf16 (bit patterns or a torch bf16 tensor) -> float64, exactly; float inputs pass through as float64."""
+    if hasattr(a, "dtype") and str(a.dtype) in ("torch.float64", "torch.float32"):
+        return a.double().numpy()
+    if isinstance(a, np.ndarray) and a.dtype.kind == "f":
+        return a.astype(np.float64)
+    return (_bits(a).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def head_projection(A, B):
+    """Per-head projection in fp64: C[m, hd, n] = sum_k A[m, hd, k] * B[hd, n, k].
+
+    A [M, H, K] and B [H, N, K] as bf16 (bit patterns or torch bf16 tensors; any
+    leading dims of A are flattened into M). With A = q_nope [b,s,h,d] and
+    B = Wk [h,k,d] this is the query absorption Q Wk^T; with A = o_lat
+    [b,s,h,k] and B = Wv^T [h,d,k] it is the output decompression O_lat Wv
+    ("Mla Analysis" skill page, "Absorption Trick (FlashMLA)"). Returns
+    float64 [..., H, N] with A's leading shape.
+    """
+    a = _wide(A)
+    b = _wide(B)
+    lead = a.shape[:-2]
+    h, k = a.shape[-2], a.shape[-1]
+    assert b.shape[0] == h and b.shape[2] == k
+    a2 = a.reshape(-1, h, k)
+    c = np.einsum("mhk,hnk->mhn", a2, b)
+    return c.reshape(*lead, h, b.shape[1])

@@ -37,13 +37,20 @@ def lib():
     L.mla_decode_unabsorbed_workspace_size.argtypes = [I] * 7
     L.mla_decode_unabsorbed_workspace_size.restype = Z
     L.mla_decode_unabsorbed.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, P]
+    L.mla_absorb_queries.argtypes = [P, P, P, I, I, I, I, I, P]
+    L.mla_decompress_output.argtypes = [P, P, P, I, I, I, I, I, P]
+    L.mla_decode_split_cache_workspace_size.argtypes = [I] * 6
+    L.mla_decode_split_cache_workspace_size.restype = Z
+    L.mla_decode_split_cache.argtypes = [P] * 9 + [I] * 5 + [F, P, P, P, Z, I, P]
     return L
 
 
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     for n in ("mla_decode", "gqa_decode", "mla_decode_workspace_size", "gqa_decode_workspace_size",
-              "mla_decode_unabsorbed", "mla_decode_unabsorbed_workspace_size", "da_status_string", "da_version"):
+              "mla_decode_unabsorbed", "mla_decode_unabsorbed_workspace_size", "mla_absorb_queries",
+              "mla_decompress_output", "mla_decode_split_cache", "mla_decode_split_cache_workspace_size",
+              "da_status_string", "da_version"):
         assert n in names
 
 
@@ -152,3 +159,43 @@ def test_unabsorbed_workspace_size(lib):
     sz = lib.mla_decode_unabsorbed_workspace_size(b, s, h, 192, 128, 512, w)
     # per partial slot and query row: 128 bf16 outputs and one fp32 lse
     assert (b + w) * s * h * (2 * 128 + 4) <= sz < (b + w) * s * h * (2 * 128 + 4) + 64 * 1024
+
+
+@pytest.mark.parametrize("fn", ["mla_absorb_queries", "mla_decompress_output"])
+@pytest.mark.parametrize("args, code", [
+    ((None, FAKE, FAKE, 2, 1, 4, 128, 512), 1), ((FAKE, None, FAKE, 2, 1, 4, 128, 512), 1),
+    ((FAKE, FAKE, None, 2, 1, 4, 128, 512), 1), ((FAKE, FAKE, FAKE, 0, 1, 4, 128, 512), 1),
+    ((FAKE, FAKE, FAKE, 2, -1, 4, 128, 512), 1), ((FAKE, FAKE, FAKE, 2, 1, 0, 128, 512), 1),
+    ((ctypes.c_void_p(0x100004), FAKE, FAKE, 2, 1, 4, 128, 512), 1),
+    ((FAKE, FAKE, ctypes.c_void_p(0x100008), 2, 1, 4, 128, 512), 1),
+])
+def test_projection_rejects(lib, fn, args, code):
+    assert getattr(lib, fn)(*args, None) == code
+
+
+def test_projection_contracted_width_multiple_of_32(lib):
+    # the contracted width is d for the queries (5th argument after b, s, h) and k for the output
+    assert lib.mla_absorb_queries(FAKE, FAKE, FAKE, 2, 1, 4, 100, 512, None) == 2
+    assert lib.mla_decompress_output(FAKE, FAKE, FAKE, 2, 1, 4, 500, 128, None) == 2
+
+
+def split_call(lib, **kw):
+    a = dict(b=2, s=2, h=8, o=256, n=64, scale=0.1, ws=FAKE, wsb=0, nw=0, qn=FAKE)
+    a.update(kw)
+    return lib.mla_decode_split_cache(a["qn"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["b"], a["s"], a["h"],
+                                      a["o"], a["n"], a["scale"], FAKE, FAKE, a["ws"], a["wsb"], a["nw"], None)
+
+
+@pytest.mark.parametrize("kw, code", [({"b": 0}, 1), ({"s": 65, "n": 100}, 2), ({"s": 80}, 1), ({"o": 0}, 1),
+                                      ({"qn": None}, 1), ({"scale": -1.0}, 1), ({}, 3)])
+def test_split_cache_rejects(lib, kw, code):
+    assert split_call(lib, **kw) == code
+
+
+def test_split_cache_workspace_covers_both_parts(lib):
+    b, s, h, o, n = 2, 2, 8, 256, 64
+    sz = lib.mla_decode_split_cache_workspace_size(b, s, h, o, n, 0)
+    parts = (lib.mla_decode_workspace_size(b, 1, s * h, 512, 64, o, 0)
+             + lib.mla_decode_unabsorbed_workspace_size(b, s, h, 192, 128, n, 0))
+    assert sz >= parts + b * s * h * (2 * 512 * 2 + 192 * 2 + 2 * 128 * 2 + 8)
+    assert lib.mla_decode_split_cache_workspace_size(b, 80, h, o, n, 0) == 0

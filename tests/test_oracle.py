@@ -126,6 +126,42 @@ def test_absorption_identity(oracle_mod):
         np.testing.assert_allclose(lse[0, 0, hh], l_h[0], atol=1e-11, rtol=0)
 
 
+def test_head_projection_identity_and_absorption(oracle_mod):
+    """The per-head projections (query absorption, output decompression):
+    identity weights reproduce their input, and absorbed attention taken through
+    both projections equals un-absorbed attention on K_h = Z Wk, V_h = Z Wv
+    ("Mla Analysis" skill page, "Absorption Trick (FlashMLA)"). Integer-valued
+    weights and queries keep q_lat exact in bf16."""
+    g = torch.Generator().manual_seed(31)
+    A = torch.randn(2, 3, 4, 32, generator=g).to(torch.bfloat16)
+    eye = torch.zeros(4, 40, 32)
+    eye[:, :32, :] = torch.eye(32)
+    C = oracle_mod.head_projection(A, eye.to(torch.bfloat16))
+    np.testing.assert_array_equal(C[..., :32], bf16_to_f64(A).numpy())
+    np.testing.assert_array_equal(C[..., 32:], 0.0)
+
+    h, k, p, d, dv, t = 8, 64, 16, 32, 24, 80
+    Z = torch.randn(1, t, k + p, generator=g).to(torch.bfloat16)
+    Wk = torch.randint(-1, 2, (h, k, d), generator=g).to(torch.bfloat16)
+    WvT = torch.randint(-1, 2, (h, dv, k), generator=g).to(torch.bfloat16)
+    Qh = torch.randint(-1, 2, (1, 1, h, d), generator=g).to(torch.bfloat16)
+    q_rope = torch.randn(1, 1, h, p, generator=g).to(torch.bfloat16)
+    q_lat64 = oracle_mod.head_projection(Qh, Wk)                 # [1, 1, h, k]
+    q_lat = torch.from_numpy(q_lat64).to(torch.bfloat16)
+    assert np.array_equal(bf16_to_f64(q_lat).numpy(), q_lat64)   # exact in bf16
+    scale = 1.0 / math.sqrt(48)
+    out_lat, lse = oracle_mod.mla(q_lat, q_rope, Z, torch.tensor([t], dtype=torch.int32), scale)
+    out = oracle_mod.head_projection(out_lat, WvT)                # [1, 1, h, dv]
+    Zl, kpe = bf16_to_f64(Z[0, :, :k]), bf16_to_f64(Z[0, :, k:])
+    for hh in range(h):
+        K_h = torch.cat([Zl @ bf16_to_f64(Wk[hh]), kpe], -1)
+        V_h = Zl @ bf16_to_f64(WvT[hh]).T
+        Q_full = torch.cat([bf16_to_f64(Qh[0, 0, hh]), bf16_to_f64(q_rope[0, 0, hh])])[None]
+        o_h, l_h = oracle_mod.attn_generic(Q_full.numpy(), K_h.numpy(), V_h.numpy(), [t], scale)
+        np.testing.assert_allclose(out[0, 0, hh], o_h[0], atol=1e-10, rtol=1e-12)
+        np.testing.assert_allclose(lse[0, 0, hh], l_h[0], atol=1e-11, rtol=0)
+
+
 def test_mla_single_visible_row(oracle_mod):
     """With one visible cache row the output is that row's latent part and lse its score."""
     shape, ql, qr, c, _ = rand_mla(1, 1, 3, 16, 8, 10, seed=7)

@@ -435,6 +435,111 @@ def test_mla_unabsorbed_matches_absorbed(da):
     assert (l_u.cpu() - l_a.cpu()).abs().max().item() <= 3e-2
 
 
+# ------------------------------------------------------------------ per-head projections
+PROJ_CASES = [
+    # (kind, b, s, h, d, k)
+    ("absorb", 3, 2, 5, 128, 512),       # M = 6: one partial M tile
+    ("absorb", 2, 33, 3, 128, 192),      # M = 66: a ragged second M tile, N = 192
+    ("decompress", 2, 33, 3, 128, 512),  # M = 66, N = 128
+    ("decompress", 1, 1, 7, 100, 256),   # N = 100: a ragged N tile
+    ("absorb", 32, 4, 128, 128, 512),    # DeepSeek-V3-like, s = 4
+    ("decompress", 32, 4, 128, 128, 512),
+]
+
+
+@pytest.mark.parametrize("case", PROJ_CASES, ids=lambda c: "%s_b%d_s%d_h%d_d%d_k%d" % c)
+def test_head_projection(da, oracle_mod, case):
+    kind, b, s, h, d, k = case
+    gen = torch.Generator().manual_seed(500 + b + s + h + d + k)
+    if kind == "absorb":
+        A = torch.randn((b, s, h, d), generator=gen).to(torch.bfloat16)
+        W = (torch.randn((h, k, d), generator=gen) / math.sqrt(d)).to(torch.bfloat16)
+        out = da.mla_absorb_queries(A.to(dev()), W.to(dev()))
+    else:
+        A = torch.randn((b, s, h, k), generator=gen).to(torch.bfloat16)
+        W = (torch.randn((h, d, k), generator=gen) / math.sqrt(k)).to(torch.bfloat16)
+        out = da.mla_decompress_output(A.to(dev()), W.to(dev()))
+    torch.cuda.synchronize()
+    ref = oracle_mod.head_projection(A, W)
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert got.shape == ref.shape
+    err = np.abs(got - ref).max()
+    assert err <= 1e-2 * np.abs(ref).max(), "%s: max|d| %.3e vs max|ref| %.3e" % (case, err, np.abs(ref).max())
+
+
+def test_absorbed_path_through_projections_matches_unabsorbed(da):
+    """Q-absorption -> absorbed decode -> output decompression, all on the GPU,
+    against un-absorbed decode on K = [Z Wk | Z_rope], V = Z Wv (GPU against
+    GPU, up to the bf16 roundings on either path)."""
+    b, s, h, t, kl, dn, p = 2, 3, 8, 256, 512, 128, 64
+    gen = torch.Generator().manual_seed(78)
+    Z = torch.randn((b, t, kl + p), generator=gen).to(torch.bfloat16)
+    Wk = (torch.randn((h, kl, dn), generator=gen) / math.sqrt(kl)).to(torch.bfloat16)
+    WvT = (torch.randn((h, dn, kl), generator=gen) / math.sqrt(kl)).to(torch.bfloat16)
+    qn = torch.randn((b, s, h, dn), generator=gen).to(torch.bfloat16)
+    qr = torch.randn((b, s, h, p), generator=gen).to(torch.bfloat16)
+    sl = torch.tensor([256, 100], dtype=torch.int32)
+    scale = 1.0 / math.sqrt(dn + p)
+    Zf = Z.float()
+    K = torch.cat([torch.einsum("btk,hkd->bthd", Zf[..., :kl], Wk.float()),
+                   Zf[..., kl:].unsqueeze(2).expand(b, t, h, p)], -1)
+    V = torch.einsum("btk,hdk->bthd", Zf[..., :kl], WvT.float())
+    d = dev()
+    g16 = lambda x: x.to(torch.bfloat16).contiguous().to(d)  # noqa: E731
+    q_lat = da.mla_absorb_queries(g16(qn), g16(Wk))
+    o_lat, l_a = da.mla_decode(q_lat, g16(qr), g16(Z), sl.to(d), scale)
+    o_a = da.mla_decompress_output(o_lat, g16(WvT))
+    o_u, l_u = da.mla_decode_unabsorbed(g16(torch.cat([qn.float(), qr.float()], -1)), g16(K), g16(V), sl.to(d), scale)
+    torch.cuda.synchronize()
+    o_a, o_u = o_a.float().cpu(), o_u.float().cpu()
+    assert (o_a - o_u).abs().max().item() <= 5e-2 * o_u.abs().max().item()
+    assert (l_a.cpu() - l_u.cpu()).abs().max().item() <= 3e-2
+
+
+# ------------------------------------------------------------------ split latent / decompressed cache
+@pytest.mark.parametrize("case", [(2, 3, 4, [100, 37], [20, 5], 128, 32, 0),
+                                  (1, 1, 8, [300], [1], 320, 4, 0),
+                                  (3, 2, 2, [0, 64, 500], [40, 2, 9], 512, 48, 6)],
+                         ids=lambda c: "b%d_s%d_h%d_w%d" % (c[0], c[1], c[2], c[7]))
+def test_mla_split_cache(da, oracle_mod, case):
+    """Old rows latent (absorbed, through both projections), new rows
+    decompressed (un-absorbed), merged: against the oracle's textbook attention
+    over all rows, old keys and values Z Wk / Z Wv and new ones as given.
+    Integer-valued weights and q_nope keep q_lat exact in bf16."""
+    b, s, h, o_l, n_l, o_max, n_max, workers = case
+    gen = torch.Generator().manual_seed(600 + b + s + h)
+    Z = torch.randn((b, o_max, 576), generator=gen).to(torch.bfloat16)
+    Wk = torch.randint(-1, 2, (h, 512, 128), generator=gen).to(torch.bfloat16)
+    WvT = torch.randint(-1, 2, (h, 128, 512), generator=gen).to(torch.bfloat16)
+    qn = torch.randint(-1, 2, (b, s, h, 128), generator=gen).to(torch.bfloat16)
+    qr = torch.randn((b, s, h, 64), generator=gen).to(torch.bfloat16)
+    kn = torch.randn((b, n_max, h, 192), generator=gen).to(torch.bfloat16)
+    vn = (4.0 * torch.randn((b, n_max, h, 128), generator=gen)).to(torch.bfloat16)
+    so, sn = torch.tensor(o_l, dtype=torch.int32), torch.tensor(n_l, dtype=torch.int32)
+    scale = 1.0 / math.sqrt(192) / 8.0
+    d = dev()
+    out, lse = da.mla_decode_split_cache(qn.to(d), qr.to(d), Wk.to(d), WvT.to(d), Z.to(d), so.to(d), kn.to(d),
+                                         vn.to(d), sn.to(d), scale, num_workers=workers)
+    torch.cuda.synchronize()
+    f64 = lambda x: x.double()  # noqa: E731
+    ref_o = np.zeros((b, s, h, 128))
+    ref_l = np.full((b, s, h), -np.inf)
+    for bq in range(b):
+        o, n = o_l[bq], n_l[bq]
+        for hh in range(h):
+            K_old = torch.cat([f64(Z[bq, :o, :512]) @ f64(Wk[hh]), f64(Z[bq, :o, 512:])], -1)
+            V_old = f64(Z[bq, :o, :512]) @ f64(WvT[hh]).T
+            K = torch.cat([K_old, f64(kn[bq, :n, hh])], 0)
+            V = torch.cat([V_old, f64(vn[bq, :n, hh])], 0)
+            Q = torch.cat([f64(qn[bq, :, hh]), f64(qr[bq, :, hh])], -1)
+            n_vis = [o + max(0, n - s + i + 1) for i in range(s)]
+            if o + n == 0:
+                continue
+            ro, rl = oracle_mod.attn_generic(Q.numpy(), K.numpy(), V.numpy(), n_vis, scale)
+            ref_o[bq, :, hh], ref_l[bq, :, hh] = ro, rl
+    compare(out.cpu(), lse.cpu(), ref_o, ref_l, "split cache %s" % (case,))
+
+
 @pytest.fixture(scope="module")
 def gqa_long_case(oracle_mod):
     """One 262,144-token sequence at 24 query / 4 KV heads, d = 256, with the
