@@ -516,16 +516,30 @@ da_status mla_decode_unabsorbed(const uint16_t *q, const uint16_t *k_cache, cons
 }
 
 // ------------------------------------------------------------------ per-head projections
+#ifndef PROJ_BLOCKS_PER_CU
+#define PROJ_BLOCKS_PER_CU 2  // blocks per CU of the tile loop
+#endif
 static da_status head_gemm(const uint16_t *a, const uint16_t *bw, uint16_t *c, int m, int h, int n, int k,
                            void *stream)
 {
     if (!a || !bw || !c || m <= 0 || h <= 0 || n <= 0 || k <= 0) return DA_ERR_INVALID_ARG;
-    if (k % 32 != 0 || (n + da::kGemmTile - 1) / da::kGemmTile > 65535 ||
-        (m + da::kGemmTile - 1) / da::kGemmTile > 65535)
-        return DA_ERR_UNSUPPORTED;
+    if (k % 32 != 0) return DA_ERR_UNSUPPORTED;
     if (!aligned16(a) || !aligned16(bw) || !aligned16(c)) return DA_ERR_INVALID_ARG;
-    const dim3 grid(h, (n + da::kGemmTile - 1) / da::kGemmTile, (m + da::kGemmTile - 1) / da::kGemmTile);
-    hipLaunchKernelGGL(da::head_gemm_kernel, grid, dim3(256), 0, (hipStream_t)stream, a, bw, c, m, h, n, k);
+    const long tiles = (long)h * ((n + da::kGemmTile - 1) / da::kGemmTile) * ((m + da::kGemmTile - 1) / da::kGemmTile);
+    const int cus = current_cu_count();
+    if (tiles < 2L * cus) {
+        // few tiles: the four waves of a block split each tile's contraction
+        const long want = 2L * cus;
+        const unsigned grid = (unsigned)(tiles < want ? tiles : want);
+        hipLaunchKernelGGL(da::head_gemm_kernel<4>, dim3(grid), dim3(256), 0, (hipStream_t)stream, a, bw, c, m, h, n,
+                           k);
+    } else {
+        const long want = (long)PROJ_BLOCKS_PER_CU * cus;
+        const long blocks = (tiles + 3) / 4;  // four tiles (one per wave) per block
+        const unsigned grid = (unsigned)(blocks < want ? blocks : want);
+        hipLaunchKernelGGL(da::head_gemm_kernel<1>, dim3(grid), dim3(256), 0, (hipStream_t)stream, a, bw, c, m, h, n,
+                           k);
+    }
     return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

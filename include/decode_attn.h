@@ -170,8 +170,7 @@ da_status mla_decode_unabsorbed(const uint16_t *q, const uint16_t *k_cache, cons
  * width (d for the queries, k for the output) must be a multiple of 32 and all
  * three tensors 16-byte aligned. No workspace; queued asynchronously on `stream`.
  * Errors: DA_ERR_INVALID_ARG (null pointer, dimension <= 0, misaligned input),
- * DA_ERR_UNSUPPORTED (contracted width not a multiple of 32, more than 65535
- * tiles of 64 output columns or of 64 query tokens).
+ * DA_ERR_UNSUPPORTED (contracted width not a multiple of 32).
  */
 da_status mla_absorb_queries(const uint16_t *q_nope, const uint16_t *w_k, uint16_t *q_lat, int b, int s, int h,
                              int d, int k, void *stream);
