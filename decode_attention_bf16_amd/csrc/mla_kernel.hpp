@@ -98,15 +98,16 @@ struct MlaCfg {
 // c ^ tile_swz(r) (the low three bits, i.e. within its 128-byte group). A tile
 // row is an odd multiple of 128 bytes, so with 64 four-byte banks the row's
 // parity picks the bank half and the swizzle the 16-byte group inside it. The
-// map is linear in bits 1..3 of r (columns 3, 4, 5 for bits 1, 2, 3) and was
-// chosen, by checking every access pattern of this kernel on the CPU, so that
-// the 16-row score reads (ds_read_b128) and the 4-row transposing reads
-// (ds_read_b64_tr_b16) hit 64 distinct banks under every plausible grouping of
-// the 64 lanes into 16- or 32-lane passes (contiguous, or lanes l and l+32).
+// map is linear in bits 1..3 of r and was chosen, by modelling every access
+// pattern of this kernel on the CPU, so that each pass of the LDS (16 lanes of
+// a ds_read_b128, 32 lanes of a ds_read_b64_tr_b16; contiguous lanes, or lanes
+// l and l+32 together) touches every bank at most once: the 16-row score reads
+// need it bijective on bits 1..3, and the transposing reads, whose 32-lane pass
+// spans four consecutive rows, need bit 2 of the result to follow bit 1 of r.
 __device__ __forceinline__ int tile_swz(int r)
 {
     const int i0 = (r >> 1) & 1, i1 = (r >> 2) & 1, i2 = (r >> 3) & 1;
-    return (i0 ^ i2) | (i0 << 1) | ((i1 ^ i2) << 2);
+    return i0 | ((i1 ^ i2) << 1) | ((i0 ^ i2) << 2);
 }
 
 // Eight bf16 values times a power of two (exact unless the result leaves the
