@@ -192,6 +192,20 @@ __device__ __forceinline__ void lds_dma16(const u32x4 &rsrc, const DA_LDS void *
                  : "memory");
 }
 
+// The same copy with the non-temporal hint (nt), for data that exactly one
+// block reads once: the lines are not kept in the caches for reuse, which
+// leaves the L2 and the last-level cache to the rest of the stream. Data that
+// several blocks read (an MLA tile shared by the row blocks of a worker) keeps
+// the default policy.
+__device__ __forceinline__ void lds_dma16_stream(const u32x4 &rsrc, const DA_LDS void *lds_base, uint32_t voffset)
+{
+    const uint32_t m0 = (uint32_t)(uintptr_t)lds_base;
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                 :
+                 : "v"(voffset), "s"(rsrc), "{m0}"(m0)
+                 : "memory");
+}
+
 __device__ __forceinline__ int clamp_len(int len, int t_max)
 {
     return len < 0 ? 0 : (len > t_max ? t_max : len);

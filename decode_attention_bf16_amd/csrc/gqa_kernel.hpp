@@ -407,7 +407,8 @@ __global__ void __launch_bounds__(64 * HPB, 1)
             const uint16_t *base = (is_k ? kc : vc) + (size_t)bq * t_max * te;
             const u32x4 rsrc = raw_buffer_rsrc(base, (uint32_t)(L * te * 2));
             const uint32_t off = (uint32_t)(((tok0 + tk) * te + hb * C::HPB * (is_k ? D : DV)) * 2 + c * 16);
-            lds_dma16(rsrc, dst + cp * 1024, off);
+            // each K/V byte is read by this wave's block only: a streaming copy
+            lds_dma16_stream(rsrc, dst + cp * 1024, off);
         }
     };
 
