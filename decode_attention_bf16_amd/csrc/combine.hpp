@@ -103,7 +103,11 @@ __device__ __forceinline__ void combine_write(uint16_t *__restrict__ out, float 
 
 // One wave per query row (grid-stride over rows); DV output columns spread
 // over the 64 lanes. A launch of a few blocks per CU keeps the cost low when
-// most rows belong to single-segment sequences and are skipped.
+// most rows belong to single-segment sequences and are skipped. The kernel is
+// bound by the latency of its dependent loads, so the chain is kept short: the
+// first row's segment range loads together with the plan header, and a row of
+// at most four segments loads its segment lse values (every lane reads the
+// same ones, so no cross-lane maximum is needed) together with its partials.
 template <int DV>
 __global__ void __launch_bounds__(256) combine_kernel(int B, int M, const PlanHeader *__restrict__ hdr,
                                                       const int *__restrict__ slot_start,
@@ -112,25 +116,59 @@ __global__ void __launch_bounds__(256) combine_kernel(int B, int M, const PlanHe
                                                       uint16_t *__restrict__ out, float *__restrict__ lse)
 {
     static_assert(DV % 64 == 0, "whole columns per lane");
-    if (hdr->merge_seqs == 0) return;  // every sequence was written by its one worker
+    constexpr int CPL = DV / 64;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const long rows = (long)B * M;
-    for (long row_g = (long)blockIdx.x * 4 + wave; row_g < rows; row_g += (long)gridDim.x * 4) {
+    const long first = (long)blockIdx.x * 4 + wave;
+    int s0 = 0, s1 = 0;
+    if (first < rows) {
+        const int bq = (int)(first / M);
+        s0 = slot_start[bq];
+        s1 = slot_start[bq + 1];
+    }
+    if (hdr->merge_seqs == 0) return;  // every sequence was written by its one worker
+    for (long row_g = first; row_g < rows; row_g += (long)gridDim.x * 4) {
         const int bq = (int)(row_g / M);
         const int row = (int)(row_g - (long)bq * M);
-        const int s0 = slot_start[bq];
-        const int nseg = slot_start[bq + 1] - s0;
+        if (row_g != first) {
+            s0 = slot_start[bq];
+            s1 = slot_start[bq + 1];
+        }
+        const int nseg = s1 - s0;
         if (nseg == 1) continue;
 
-        float m = -INFINITY;
-        for (int r = lane; r < nseg; r += 64) m = fmaxf(m, part_lse[(size_t)(s0 + r) * M + row]);
-        m = wave_max64(m);
-        float acc[DV / 64];
+        float acc[CPL];
 #pragma unroll
-        for (int c = 0; c < DV / 64; ++c) acc[c] = 0.f;
-        float wsum = 0.f;
-        if (m != -INFINITY) combine_accumulate<DV>(part_out, part_lse, M, row, s0, 0, 1, nseg, m, lane, acc, wsum);
+        for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+        float wsum = 0.f, m = -INFINITY;
+        if (nseg <= 4) {
+            float l[4], o[4][CPL];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                l[u] = -INFINITY;
+                if (u < nseg) {
+                    l[u] = part_lse[(size_t)(s0 + u) * M + row];
+                    load_partial<CPL>(part_out + ((size_t)(s0 + u) * M + row) * DV + lane * CPL, o[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) m = fmaxf(m, l[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (l[u] != -INFINITY) {  // empty segments (and absent ones) weigh nothing
+                    const float wgt = fast_exp2(l[u] - m);
+                    wsum += wgt;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) acc[c] += wgt * o[u][c];
+                }
+            }
+        } else {
+            for (int r = lane; r < nseg; r += 64) m = fmaxf(m, part_lse[(size_t)(s0 + r) * M + row]);
+            m = wave_max64(m);
+            if (m != -INFINITY)
+                combine_accumulate<DV>(part_out, part_lse, M, row, s0, 0, 1, nseg, m, lane, acc, wsum);
+        }
         combine_write<DV>(out, lse, row_g, lane, acc, wsum, m);
     }
 }
