@@ -194,6 +194,49 @@ def time_parts(parts, steps, warmup):
     return wall, per
 
 
+def measured_ceilings(dev, reps=20):
+    """What this GPU attains, as reference points for the ridge (not the decode path): HBM bytes per
+    second of a 1 GiB device-to-device copy (read + write), and bf16 FLOP/s of an 8192^3 GEMM through
+    the vendor library."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    x = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    y = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    res = {}
+    for name, fn, work in (("copy", lambda: b.copy_(a), 2.0 * a.numel()),
+                           ("gemm", lambda: torch.matmul(x, y), 2.0 * 8192 ** 3)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = work * reps / (e0.elapsed_time(e1) / 1e3)
+    del a, b, x, y
+    torch.cuda.empty_cache()
+    return res["copy"], res["gemm"]
+
+
+def ridge_summary(us, dev):
+    """Where the MLA s-sweep crosses the ridge: analytic s* at the published ceilings, at the ceilings
+    measured here, and at this kernel's own best matrix rate; plus the time of each s relative to s=1
+    (flat below the crossing, proportional to s above it)."""
+    sh = wl.mla_mtp(1)
+    bw, fl = measured_ceilings(dev)
+    best = max(tf for _, tf in us.values()) * 1e12
+    cross = lambda f, b: round(cm.mla_ridge_crossing_s(sh.h, sh.k, sh.p, sh.t_max, peak_flops=f, bw=b), 3)
+    return {"sweep_summary": "mla_mtp ridge crossing (b=32, h=128, k=512, p=64, t=4096)",
+            "spec_ridge_flop_per_byte": round(RIDGE, 1),
+            "spec_crossing_s": cross(cm.MI355X_BF16_FLOPS, cm.MI355X_HBM_BYTES_PER_S),
+            "measured_copy_tbs": round(bw / 1e12, 3), "measured_gemm_tflops": round(fl / 1e12, 1),
+            "measured_ridge_flop_per_byte": round(fl / bw, 1), "measured_crossing_s": cross(fl, bw),
+            "kernel_best_tflops": round(best / 1e12, 1), "kernel_crossing_s": cross(best, bw),
+            "time_vs_s1": {str(s): round(t / us[1][0], 3) for s, (t, _) in sorted(us.items())}}
+
+
 def cpu_baseline(parts, fraction):
     import oracle
     oracle.build(force=False)
@@ -355,10 +398,12 @@ def main():
         return
 
     if args.sweep:
+        us = {}
         for s in wl.MTP_SWEEP:
             p = Part("mla_s%d" % s, "mla", wl.mla_mtp(s), dev)
             wall, per = time_parts([p], args.steps, args.warmup)
             sec = per[p.name]
+            us[s] = (sec * 1e6, p.cost.flops / sec / 1e12)
             print(json.dumps({"sweep": "mla_mtp", "s": s, "us": round(sec * 1e6, 2),
                               "tflops": round(p.cost.flops / sec / 1e12, 2),
                               "tbs": round(p.cost.bytes / sec / 1e12, 3), "ai": round(p.cost.ai, 1),
@@ -366,6 +411,7 @@ def main():
                               "roofline_frac": round(p.t_min / sec, 4)}), flush=True)
             del p
             torch.cuda.empty_cache()
+        print(json.dumps(ridge_summary(us, dev)), flush=True)
         return
 
     parts = [Part("gqa", "gqa", wl.GQA_LAYER, dev, args.gqa_path), Part("mla_s1", "mla", wl.MLA_DSV3, dev),
