@@ -196,15 +196,16 @@ def time_parts(parts, steps, warmup):
 
 def measured_ceilings(dev, reps=20):
     """What this GPU attains, as reference points for the ridge (not the decode path): HBM bytes per
-    second of a 1 GiB device-to-device copy (read + write), and bf16 FLOP/s of an 8192^3 GEMM through
+    second of a 1 GiB device-to-device copy (read + write), and bf16 FLOP/s of a 12288^3 GEMM through
     the vendor library."""
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
-    x = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
-    y = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    n = 12288
+    x = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    y = torch.randn(n, n, device=dev).to(torch.bfloat16)
     res = {}
     for name, fn, work in (("copy", lambda: b.copy_(a), 2.0 * a.numel()),
-                           ("gemm", lambda: torch.matmul(x, y), 2.0 * 8192 ** 3)):
+                           ("gemm", lambda: torch.matmul(x, y), 2.0 * n ** 3)):
         for _ in range(3):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
