@@ -73,16 +73,35 @@ bool log_plan()
 // ------------------------------------------------------------------ MLA
 int mla_row_blocks(int s, int h) { return (s * h + da::kMlaRows - 1) / da::kMlaRows; }
 
+// Workers (split-KV segments over the tile sequence) for the MLA tile kernel.
+// One block per CU is resident, so the units = workers x row blocks run in
+// waves of `cus`; a block costs its fixed part (first loads and final stores,
+// about kMlaFixedSteps tile steps) plus one step per tile. The count that
+// minimises waves x (fixed + tiles per worker) is taken, with the tiles
+// estimated from t_max (the lengths are on the device). For the power-of-two
+// row-block counts this is cus / row_blocks; for others (e.g. 96 row blocks at
+// s = 48, h = 128) it fills the CUs in several waves instead of leaving some idle.
+constexpr int kMlaFixedSteps = 12;
+
 int mla_workers(int b, int s, int h, int t_max, int requested)
 {
     if (requested > 0) return requested;
     const int rb = mla_row_blocks(s, h);
-    int w = current_cu_count() / rb;
-    if (w < 1) w = 1;
+    const int cus = current_cu_count();
     // never more workers than tiles could exist
     const long max_tiles = (long)b * ((t_max + da::kMlaTile - 1) / da::kMlaTile);
-    if ((long)w > max_tiles) w = (int)max_tiles;
-    return w < 1 ? 1 : w;
+    const long w_hi = std::min<long>(max_tiles, std::max<long>(1, 4L * cus / rb));
+    long best_w = 1;
+    double best = -1.0;
+    for (long w = 1; w <= w_hi; ++w) {
+        const long waves = (w * rb + cus - 1) / cus;
+        const double cost = (double)waves * (kMlaFixedSteps + (double)((max_tiles + w - 1) / w));
+        if (best < 0.0 || cost < best) {
+            best = cost;
+            best_w = w;
+        }
+    }
+    return (int)best_w;
 }
 
 bool mla_supported(int k, int p)
@@ -506,6 +525,9 @@ da_status mla_decode_unabsorbed(const uint16_t *q, const uint16_t *k_cache, cons
                             part_out, part_lse, workers, st_);
     else if (s <= 32)
         e = launch_unabs<2>(q, k_cache, v_cache, seqlens, b, s, h, t_max, sl2, out, lse, hdr, tile_start, slot_start,
+                            part_out, part_lse, workers, st_);
+    else if (s <= 48)  // three 16-row blocks: s = 33..48 without padding to 64 rows
+        e = launch_unabs<3>(q, k_cache, v_cache, seqlens, b, s, h, t_max, sl2, out, lse, hdr, tile_start, slot_start,
                             part_out, part_lse, workers, st_);
     else
         e = launch_unabs<4>(q, k_cache, v_cache, seqlens, b, s, h, t_max, sl2, out, lse, hdr, tile_start, slot_start,

@@ -385,7 +385,9 @@ UNABS_SMALL = [
     (3, 3, 8, 100, [100, 2, 0], 0),       # drafts, L < s, an empty sequence
     (1, 16, 4, 200, [200], 3),            # 16 drafts: one 16-row block
     (2, 20, 2, 130, [130, 64], 2),        # 20 drafts: two row blocks
-    (1, 40, 2, 300, [300], 5),            # 40 drafts: four row blocks
+    (1, 40, 2, 300, [300], 5),            # 40 drafts: three row blocks
+    (2, 48, 2, 260, [260, 100], 3),       # 48 drafts: three full row blocks
+    (1, 56, 2, 300, [300], 4),            # 56 drafts: four row blocks
     (2, 1, 5, 1000, [1000, 999], 0),      # odd head count: the last head block has one active wave
     (2, 2, 3, 700, [700, 350], 40),       # many segments per row (block-per-row combine)
 ]
