@@ -267,6 +267,9 @@ hipError_t dispatch_gqa_mfma(int rows, const uint16_t *q, const uint16_t *k, con
     if (rows <= 32 || D == 256)
         return launch_gqa_mfma<D, 2>(q, k, v, seqlens, b, s, hq, hkv, t_max, scale_log2, out, lse, hdr, tile_start,
                                      slot_start, part_out, part_lse, workers, stream);
+    if (rows <= 48)  // three 16-row blocks: 33..48 rows without padding to 64 (d = 256 stops at 32 rows)
+        return launch_gqa_mfma<D, (D == 256 ? 2 : 3)>(q, k, v, seqlens, b, s, hq, hkv, t_max, scale_log2, out, lse,
+                                                      hdr, tile_start, slot_start, part_out, part_lse, workers, stream);
     return launch_gqa_mfma<D, (D == 256 ? 2 : 4)>(q, k, v, seqlens, b, s, hq, hkv, t_max, scale_log2, out, lse, hdr,
                                                   tile_start, slot_start, part_out, part_lse, workers, stream);
 }

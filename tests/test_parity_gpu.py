@@ -283,6 +283,9 @@ GQA_SMALL = [
     (2, 1, 10, 5, 128, 90, [90, 40]),        # 5 KV heads: the second head block has one active wave
     (2, 2, 18, 9, 64, 80, [80, 3]),          # d = 64, 9 KV heads over two head blocks
     (2, 2, 24, 4, 256, 150, [150, 77]),      # groups of 6 at d = 256 (12 rows per KV head)
+    (2, 5, 16, 2, 128, 160, [160, 77]),      # group 8 x 5 drafts = 40 rows: three row blocks
+    (1, 3, 48, 4, 64, 90, [90]),             # group 12 x 3 drafts = 36 rows at d = 64
+    (2, 6, 32, 4, 128, 120, [120, 5]),       # 48 rows: three full row blocks, L < s in one sequence
 ]
 
 
