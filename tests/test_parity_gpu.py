@@ -255,6 +255,12 @@ def test_mla_ragged_full_size(da, oracle_mod):
     full_size_mla(da, oracle_mod, wl.MLA_RAGGED, n_rows=96)
 
 
+def test_mla_s48_full_size(da, oracle_mod):
+    """48 drafts at the DeepSeek-V3-like shapes: 96 row blocks per sequence, for which the automatic
+    worker count runs the blocks in several waves over the CUs."""
+    full_size_mla(da, oracle_mod, wl.mla_mtp(48), n_rows=128)
+
+
 # ------------------------------------------------------------------ GQA
 def run_gqa(da, shape, tensors, num_workers=0, path=0):
     q, k, v, sl = tensors
