@@ -81,6 +81,8 @@ int mla_row_blocks(int s, int h) { return (s * h + da::kMlaRows - 1) / da::kMlaR
 // estimated from t_max (the lengths are on the device). For the power-of-two
 // row-block counts this is cus / row_blocks; for others (e.g. 96 row blocks at
 // s = 48, h = 128) it fills the CUs in several waves instead of leaving some idle.
+// Within one wave count the cost falls as workers grow, so only the largest
+// count of each wave count (up to four waves) and the cap are candidates.
 constexpr int kMlaFixedSteps = 12;
 
 int mla_workers(int b, int s, int h, int t_max, int requested)
@@ -93,7 +95,8 @@ int mla_workers(int b, int s, int h, int t_max, int requested)
     const long w_hi = std::min<long>(max_tiles, std::max<long>(1, 4L * cus / rb));
     long best_w = 1;
     double best = -1.0;
-    for (long w = 1; w <= w_hi; ++w) {
+    for (int k = 1; k <= 5; ++k) {
+        const long w = k <= 4 ? std::min<long>(w_hi, std::max<long>(1, (long)k * cus / rb)) : w_hi;
         const long waves = (w * rb + cus - 1) / cus;
         const double cost = (double)waves * (kMlaFixedSteps + (double)((max_tiles + w - 1) / w));
         if (best < 0.0 || cost < best) {
