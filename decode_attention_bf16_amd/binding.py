@@ -121,6 +121,10 @@ def mla_decode_split_cache_workspace_size(b, s, h, o_max, n_max, num_workers=0) 
     return int(load_library().mla_decode_split_cache_workspace_size(b, s, h, o_max, n_max, num_workers))
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _workspace(nbytes, device, workspace):
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
@@ -130,11 +134,13 @@ def _workspace(nbytes, device, workspace):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def mla_decode(q_lat, q_rope, cache, seqlens, scale, num_workers=0, out=None, lse=None, workspace=None):
+def mla_decode(q_lat, q_rope, cache, seqlens, scale, num_workers=0, out=None, lse=None, workspace=None,
+               null_workspace=False):
     """Absorbed-latent MLA decode on the GPU.
 
     q_lat [b,s,h,k], q_rope [b,s,h,p], cache [b,t_max,k+p] (bf16), seqlens [b]
     (int32), all on one GPU. Returns (out_lat [b,s,h,k] bf16, lse [b,s,h] fp32).
+    null_workspace=True passes no workspace: one worker per sequence, no split.
     """
     lib = load_library()
     _need(q_lat, "q_lat", torch.bfloat16, 4)
@@ -159,21 +165,22 @@ def mla_decode(q_lat, q_rope, cache, seqlens, scale, num_workers=0, out=None, ls
         lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
     else:
         _need(lse, "lse", torch.float32, 3, dev)
-    nbytes = lib.mla_decode_workspace_size(b, s, h, k, p, t_max, num_workers)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = None if null_workspace else _workspace(lib.mla_decode_workspace_size(b, s, h, k, p, t_max, num_workers),
+                                                 dev, workspace)
     with torch.cuda.device(dev):
         rc = lib.mla_decode(_ptr(q_lat), _ptr(q_rope), _ptr(cache), _ptr(seqlens), b, s, h, k, p, t_max,
-                            float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
-                            int(num_workers), _stream(dev))
+                            float(scale), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), int(num_workers), _stream(dev))
     _check("mla_decode", rc)
     return out, lse
 
 
-def gqa_decode(q, k_cache, v_cache, seqlens, scale, num_workers=0, path=0, out=None, lse=None, workspace=None):
+def gqa_decode(q, k_cache, v_cache, seqlens, scale, num_workers=0, path=0, out=None, lse=None, workspace=None,
+               null_workspace=False):
     """Grouped-query decode on the GPU (MHA when hkv == hq, MQA when hkv == 1).
 
     q [b,s,hq,d], k_cache/v_cache [b,t_max,hkv,d] (bf16), seqlens [b] (int32).
     Returns (out [b,s,hq,d] bf16, lse [b,s,hq] fp32). path: 0 auto, 1 VALU, 2 MFMA.
+    null_workspace=True passes no workspace: one worker per sequence, no split.
     """
     lib = load_library()
     _need(q, "q", torch.bfloat16, 4)
@@ -195,21 +202,23 @@ def gqa_decode(q, k_cache, v_cache, seqlens, scale, num_workers=0, path=0, out=N
         lse = torch.empty((b, s, hq), dtype=torch.float32, device=dev)
     else:
         _need(lse, "lse", torch.float32, 3, dev)
-    nbytes = lib.gqa_decode_workspace_size(b, s, hq, hkv, d, t_max, num_workers, path)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = None if null_workspace else _workspace(
+        lib.gqa_decode_workspace_size(b, s, hq, hkv, d, t_max, num_workers, path), dev, workspace)
     with torch.cuda.device(dev):
         rc = lib.gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), b, s, hq, hkv, d, t_max,
-                            float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
-                            int(num_workers), int(path), _stream(dev))
+                            float(scale), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), int(num_workers), int(path),
+                            _stream(dev))
     _check("gqa_decode", rc)
     return out, lse
 
 
-def mla_decode_unabsorbed(q, k_cache, v_cache, seqlens, scale, num_workers=0, out=None, lse=None, workspace=None):
+def mla_decode_unabsorbed(q, k_cache, v_cache, seqlens, scale, num_workers=0, out=None, lse=None, workspace=None,
+                          null_workspace=False):
     """Un-absorbed MLA decode on the GPU: per-head decompressed keys and values.
 
     q [b,s,h,dqk], k_cache [b,t_max,h,dqk], v_cache [b,t_max,h,dv] (bf16), seqlens [b] (int32).
     Returns (out [b,s,h,dv] bf16, lse [b,s,h] fp32).
+    null_workspace=True passes no workspace: one worker per sequence, no split.
     """
     lib = load_library()
     _need(q, "q", torch.bfloat16, 4)
@@ -231,12 +240,12 @@ def mla_decode_unabsorbed(q, k_cache, v_cache, seqlens, scale, num_workers=0, ou
         lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
     else:
         _need(lse, "lse", torch.float32, 3, dev)
-    nbytes = lib.mla_decode_unabsorbed_workspace_size(b, s, h, dqk, dv, t_max, num_workers)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = None if null_workspace else _workspace(
+        lib.mla_decode_unabsorbed_workspace_size(b, s, h, dqk, dv, t_max, num_workers), dev, workspace)
     with torch.cuda.device(dev):
         rc = lib.mla_decode_unabsorbed(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), b, s, h, dqk, dv, t_max,
-                                       float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
-                                       int(num_workers), _stream(dev))
+                                       float(scale), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), int(num_workers),
+                                       _stream(dev))
     _check("mla_decode_unabsorbed", rc)
     return out, lse
 

@@ -126,11 +126,13 @@ hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint1
     });
     if (attr_err != hipSuccess) return attr_err;
 
-    auto *hdr = (da::PlanHeader *)(wsp + ws.header);
-    int *tile_start = (int *)(wsp + ws.tile_start);
-    int *slot_start = (int *)(wsp + ws.slot_start);
-    float *part_lse = (float *)(wsp + ws.part_lse);
-    uint16_t *part_out = (uint16_t *)(wsp + ws.part_out);
+    // no workspace: one worker per sequence, no partials and no combine
+    const bool per_seq = wsp == nullptr;
+    auto *hdr = per_seq ? nullptr : (da::PlanHeader *)(wsp + ws.header);
+    int *tile_start = per_seq ? nullptr : (int *)(wsp + ws.tile_start);
+    int *slot_start = per_seq ? nullptr : (int *)(wsp + ws.slot_start);
+    float *part_lse = per_seq ? nullptr : (float *)(wsp + ws.part_lse);
+    uint16_t *part_out = per_seq ? nullptr : (uint16_t *)(wsp + ws.part_out);
 
     const int rb = mla_row_blocks(s, h);
     const int units = workers * rb;
@@ -141,7 +143,7 @@ hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint1
     hipLaunchKernelGGL((da::mla_decode_kernel<K, P>), dim3(grid), dim3(C::THREADS), C::LDS_BYTES, stream, q_lat, q_rope,
                        cache, seqlens, b, s, h, t_max, scale_log2, rb, units, hdr, tile_start, slot_start, out, lse,
                        part_out, part_lse);
-    launch_combine<K>(b, s * h, workers, hdr, slot_start, part_out, part_lse, out, lse, stream);
+    if (!per_seq) launch_combine<K>(b, s * h, workers, hdr, slot_start, part_out, part_lse, out, lse, stream);
     return hipGetLastError();
 }
 
@@ -149,7 +151,12 @@ hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint1
 int gqa_head_blocks(int hkv) { return (hkv + 3) / 4; }
 int gqa_choose_path(int rows, int path);
 
-// Launch shape of the MFMA kernel per head dim: KV heads per block and ring depth.
+// Launch shape of the MFMA kernel: KV heads per block, row-group waves per
+// head and 16-row blocks per wave. The default block holds kBase heads with
+// one wave each (all rows of a head in that wave); when hkv is not a multiple
+// of kBase, or a head has more rows than one wave holds, a block takes the
+// fewest heads a whole LDS token row allows (kMin) and spreads each head's
+// rows over up to RG waves that share its K/V stages.
 #ifndef DA_GQA128_HPB
 #define DA_GQA128_HPB 4
 #endif
@@ -158,28 +165,55 @@ int gqa_choose_path(int rows, int path);
 #endif
 template <int D>
 struct GqaMfmaShape {
-    static constexpr int HPB = D == 128 ? DA_GQA128_HPB : 512 / D;
-    static constexpr int NST = D == 128 ? DA_GQA128_NST : 4;
+    static constexpr int kBase = D == 128 ? DA_GQA128_HPB : 512 / D;
+    static constexpr int kNst = D == 128 ? DA_GQA128_NST : 4;
+    static constexpr int kMin = D == 64 ? 2 : 1;           // a K token row of >= 256 bytes
+    static constexpr int kMaxRblk = D == 256 ? 2 : 4;      // register budget of a wave
+    static constexpr int kMaxRg = 4;
+    static constexpr int kMaxRows = 16 * kMaxRblk * kMaxRg;
 };
-template <int D, int RBLK>
-using GqaMfmaCfgFor = da::GqaMfmaCfg<D, RBLK, GqaMfmaShape<D>::HPB, GqaMfmaShape<D>::NST>;
 
-// (heads per block, resident blocks per CU) of the MFMA kernel for head dim d
-void gqa_mfma_geometry(int d, int &hpb, int &per_cu)
+struct GqaGeom {
+    int hpb = 0, rg = 0, rblk = 0;
+};
+
+int pow2ceil(int x)
 {
-    int lds = 0;
-    if (d == 64) {
-        hpb = GqaMfmaCfgFor<64, 1>::HPB;
-        lds = GqaMfmaCfgFor<64, 1>::LDS_BYTES;
-    } else if (d == 128) {
-        hpb = GqaMfmaCfgFor<128, 1>::HPB;
-        lds = GqaMfmaCfgFor<128, 1>::LDS_BYTES;
-    } else {
-        hpb = GqaMfmaCfgFor<256, 1>::HPB;
-        lds = GqaMfmaCfgFor<256, 1>::LDS_BYTES;
-    }
-    per_cu = 163840 / lds;
-    if (per_cu < 1) per_cu = 1;
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+template <int D>
+GqaGeom gqa_mfma_geom(int hkv, int rows)
+{
+    using S = GqaMfmaShape<D>;
+    const int nrb = (rows + 15) / 16;
+    if (nrb <= S::kMaxRblk && hkv % S::kBase == 0) return {S::kBase, 1, nrb};
+    int rg = std::min(S::kMaxRg, pow2ceil(nrb));
+    int rblk = (nrb + rg - 1) / rg;
+    if (rblk > S::kMaxRblk) return {};
+    return {S::kMin, rg, rblk};
+}
+
+GqaGeom gqa_geom(int d, int hkv, int rows)
+{
+    return d == 64 ? gqa_mfma_geom<64>(hkv, rows) : d == 128 ? gqa_mfma_geom<128>(hkv, rows) : gqa_mfma_geom<256>(hkv, rows);
+}
+
+int gqa_max_rows(int d)
+{
+    return d == 64 ? GqaMfmaShape<64>::kMaxRows : d == 128 ? GqaMfmaShape<128>::kMaxRows : GqaMfmaShape<256>::kMaxRows;
+}
+
+template <int D, int RBLK, int HPB, int RG>
+using GqaMfmaCfgFor = da::GqaMfmaCfg<D, RBLK, HPB, (HPB == GqaMfmaShape<D>::kBase ? GqaMfmaShape<D>::kNst : 4), D, RG>;
+
+// LDS bytes of the MFMA kernel's block for a launch shape.
+int gqa_mfma_lds(int d, const GqaGeom &g)
+{
+    const int nst = g.hpb == (d == 128 ? DA_GQA128_HPB : 512 / d) ? (d == 128 ? DA_GQA128_NST : 4) : 4;
+    return nst * 16 * g.hpb * d * 2 * 2;
 }
 
 int gqa_workers(int b, int hkv, int d, int rows, int path, int t_max, int requested)
@@ -189,9 +223,11 @@ int gqa_workers(int b, int hkv, int d, int rows, int path, int t_max, int reques
     if (gqa_choose_path(rows, path) == 0) {
         w = 2 * current_cu_count() / gqa_head_blocks(hkv);
     } else {
-        int hpb, per_cu;
-        gqa_mfma_geometry(d, hpb, per_cu);  // blocks stay resident through their LDS ring
-        w = per_cu * current_cu_count() / ((hkv + hpb - 1) / hpb);
+        const GqaGeom g = gqa_geom(d, hkv, rows);
+        // resident blocks per CU: LDS ring, and two waves per SIMD
+        int per_cu = std::min(163840 / gqa_mfma_lds(d, g), std::max(1, 8 / (g.hpb * g.rg)));
+        if (per_cu < 1) per_cu = 1;
+        w = per_cu * current_cu_count() / ((hkv + g.hpb - 1) / g.hpb);
     }
     if (w < 1) w = 1;
     const long max_tiles = (long)b * ((t_max + da::kGqaTile - 1) / da::kGqaTile);
@@ -235,46 +271,70 @@ bool dispatch_gqa_valu(int rows, const uint16_t *q, const uint16_t *k, const uin
     return false;
 }
 
-template <int D, int RBLK>
-hipError_t launch_gqa_mfma(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *seqlens, int b,
-                           int s, int hq, int hkv, int t_max, float scale_log2, uint16_t *out, float *lse,
-                           da::PlanHeader *hdr, int *tile_start, int *slot_start, uint16_t *part_out, float *part_lse,
-                           int workers, hipStream_t stream)
+struct GqaArgs {
+    const uint16_t *q, *k, *v;
+    const int32_t *seqlens;
+    int b, s, hq, hkv, t_max;
+    float scale_log2;
+    uint16_t *out;
+    float *lse;
+    da::PlanHeader *hdr;
+    int *tile_start, *slot_start;
+    uint16_t *part_out;
+    float *part_lse;
+    int workers;
+    hipStream_t stream;
+};
+
+template <int D, int RBLK, int HPB, int RG>
+hipError_t launch_gqa_mfma(const GqaArgs &a)
 {
-    using C = GqaMfmaCfgFor<D, RBLK>;
+    using C = GqaMfmaCfgFor<D, RBLK, HPB, RG>;
+    auto kern = da::gqa_mfma_kernel<D, RBLK, HPB, C::NST, D, RG>;
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
-    std::call_once(attr_once, [] {
-        attr_err = hipFuncSetAttribute((const void *)da::gqa_mfma_kernel<D, RBLK, C::HPB, C::NST>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    std::call_once(attr_once, [&] {
+        attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     });
     if (attr_err != hipSuccess) return attr_err;
-    const int hb = (hkv + C::HPB - 1) / C::HPB;
-    const int units = workers * hb;
+    const int hb = (a.hkv + HPB - 1) / HPB;
+    const int units = a.workers * hb;
     const int grid = (units + 7) / 8 * 8;
-    hipLaunchKernelGGL((da::gqa_mfma_kernel<D, RBLK, C::HPB, C::NST>), dim3(grid), dim3(C::THREADS), C::LDS_BYTES, stream, q, k, v,
-                       seqlens, b, s, hq, hkv, t_max, scale_log2, hb, units, hdr, tile_start, slot_start, out, lse,
-                       part_out, part_lse);
+    if (log_plan())
+        fprintf(stderr, "[decode_attn] gqa-mfma d=%d heads/block=%d row groups=%d row blocks/wave=%d workers=%d grid=%d lds=%d\n",
+                D, HPB, RG, RBLK, a.workers, grid, C::LDS_BYTES);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::THREADS), C::LDS_BYTES, a.stream, a.q, a.k, a.v, a.seqlens, a.b, a.s,
+                       a.hq, a.hkv, a.t_max, a.scale_log2, hb, units, a.hdr, a.tile_start, a.slot_start, a.out, a.lse,
+                       a.part_out, a.part_lse);
     return hipSuccess;
 }
 
+// The instantiated launch shapes (see gqa_mfma_geom).
 template <int D>
-hipError_t dispatch_gqa_mfma(int rows, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                             const int32_t *seqlens, int b, int s, int hq, int hkv, int t_max, float scale_log2,
-                             uint16_t *out, float *lse, da::PlanHeader *hdr, int *tile_start, int *slot_start,
-                             uint16_t *part_out, float *part_lse, int workers, hipStream_t stream)
+hipError_t dispatch_gqa_mfma(const GqaGeom &g, const GqaArgs &a)
 {
-    if (rows <= 16)
-        return launch_gqa_mfma<D, 1>(q, k, v, seqlens, b, s, hq, hkv, t_max, scale_log2, out, lse, hdr, tile_start,
-                                     slot_start, part_out, part_lse, workers, stream);
-    if (rows <= 32 || D == 256)
-        return launch_gqa_mfma<D, 2>(q, k, v, seqlens, b, s, hq, hkv, t_max, scale_log2, out, lse, hdr, tile_start,
-                                     slot_start, part_out, part_lse, workers, stream);
-    if (rows <= 48)  // three 16-row blocks: 33..48 rows without padding to 64 (d = 256 stops at 32 rows)
-        return launch_gqa_mfma<D, (D == 256 ? 2 : 3)>(q, k, v, seqlens, b, s, hq, hkv, t_max, scale_log2, out, lse,
-                                                      hdr, tile_start, slot_start, part_out, part_lse, workers, stream);
-    return launch_gqa_mfma<D, (D == 256 ? 2 : 4)>(q, k, v, seqlens, b, s, hq, hkv, t_max, scale_log2, out, lse, hdr,
-                                                  tile_start, slot_start, part_out, part_lse, workers, stream);
+    using S = GqaMfmaShape<D>;
+    constexpr int B = S::kBase, M = S::kMin;
+    if (g.hpb == B && g.rg == 1) {
+        switch (g.rblk) {
+        case 1: return launch_gqa_mfma<D, 1, B, 1>(a);
+        case 2: return launch_gqa_mfma<D, 2, B, 1>(a);
+        case 3: if constexpr (S::kMaxRblk >= 3) return launch_gqa_mfma<D, 3, B, 1>(a); break;
+        case 4: if constexpr (S::kMaxRblk >= 4) return launch_gqa_mfma<D, 4, B, 1>(a); break;
+        }
+    } else if (g.hpb == M) {
+        if (g.rg == 1 && g.rblk == 1) return launch_gqa_mfma<D, 1, M, 1>(a);
+        if (g.rg == 2 && g.rblk == 1) return launch_gqa_mfma<D, 1, M, 2>(a);
+        if (g.rg == 4) {
+            switch (g.rblk) {
+            case 1: return launch_gqa_mfma<D, 1, M, 4>(a);
+            case 2: return launch_gqa_mfma<D, 2, M, 4>(a);
+            case 3: if constexpr (S::kMaxRblk >= 3) return launch_gqa_mfma<D, 3, M, 4>(a); break;
+            case 4: if constexpr (S::kMaxRblk >= 4) return launch_gqa_mfma<D, 4, M, 4>(a); break;
+            }
+        }
+    }
+    return hipErrorInvalidValue;  // not reached: gqa_check admits only these shapes
 }
 
 // 0 = VALU dot kernel, 1 = MFMA kernel
@@ -379,14 +439,15 @@ da_status mla_decode(const uint16_t *q_lat, const uint16_t *q_rope, const uint16
 {
     da_status st = mla_check(b, s, h, k, p, t_max, num_workers);
     if (st != DA_OK) return st;
-    if (!q_lat || !q_rope || !cache || !seqlens || !out_lat || !lse || !workspace) return DA_ERR_INVALID_ARG;
+    if (!q_lat || !q_rope || !cache || !seqlens || !out_lat || !lse) return DA_ERR_INVALID_ARG;
     if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(cache) || !aligned16(out_lat))
         return DA_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255u) != 0) return DA_ERR_INVALID_ARG;
     if (!std::isfinite(scale) || !(scale > 0.f)) return DA_ERR_INVALID_ARG;
-    const int workers = mla_workers(b, s, h, t_max, num_workers);
+    // a null workspace: one worker per sequence (one split), num_workers ignored
+    const int workers = workspace ? mla_workers(b, s, h, t_max, num_workers) : b;
     const da::WsLayout ws = da::ws_layout(b, s * h, k, workers);
-    if (workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
+    if (workspace && workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
 
     const float sl2 = scale * da::kLog2e;
     hipStream_t st_ = (hipStream_t)stream;
@@ -410,8 +471,11 @@ static da_status gqa_check(int b, int s, int hq, int hkv, int d, int t_max, int 
     if (path < 0 || path > 2) return DA_ERR_INVALID_ARG;
     if (!(d == 64 || d == 128 || d == 256)) return DA_ERR_UNSUPPORTED;
     const int rows = (hq / hkv) * s;
-    if (rows > (d == 256 ? 32 : 64)) return DA_ERR_UNSUPPORTED;
-    if (gqa_choose_path(rows, path) == 0 && !gqa_valu_ok(rows)) return DA_ERR_UNSUPPORTED;
+    if (gqa_choose_path(rows, path) == 0) {
+        if (!gqa_valu_ok(rows)) return DA_ERR_UNSUPPORTED;
+    } else if (rows > gqa_max_rows(d) || gqa_geom(d, hkv, rows).hpb == 0) {
+        return DA_ERR_UNSUPPORTED;
+    }
     // one sequence's K (or V) rows must be addressable by a 32-bit buffer offset
     if ((long long)t_max * hkv * d * 2 >= (1LL << 31)) return DA_ERR_UNSUPPORTED;
     return DA_OK;
@@ -430,22 +494,24 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
 {
     da_status st = gqa_check(b, s, hq, hkv, d, t_max, num_workers, path);
     if (st != DA_OK) return st;
-    if (!q || !k_cache || !v_cache || !seqlens || !out || !lse || !workspace) return DA_ERR_INVALID_ARG;
+    if (!q || !k_cache || !v_cache || !seqlens || !out || !lse) return DA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return DA_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255u) != 0) return DA_ERR_INVALID_ARG;
     if (!std::isfinite(scale) || !(scale > 0.f)) return DA_ERR_INVALID_ARG;
     const int rows = (hq / hkv) * s;
     const int use_mfma = gqa_choose_path(rows, path);
-    const int workers = gqa_workers(b, hkv, d, rows, path, t_max, num_workers);
+    // a null workspace: one worker per sequence (one split), num_workers ignored
+    const bool per_seq = workspace == nullptr;
+    const int workers = per_seq ? b : gqa_workers(b, hkv, d, rows, path, t_max, num_workers);
     const da::WsLayout ws = da::ws_layout(b, s * hq, d, workers);
-    if (workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
+    if (!per_seq && workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
 
     char *wsp = (char *)workspace;
-    auto *hdr = (da::PlanHeader *)(wsp + ws.header);
-    int *tile_start = (int *)(wsp + ws.tile_start);
-    int *slot_start = (int *)(wsp + ws.slot_start);
-    float *part_lse = (float *)(wsp + ws.part_lse);
-    uint16_t *part_out = (uint16_t *)(wsp + ws.part_out);
+    auto *hdr = per_seq ? nullptr : (da::PlanHeader *)(wsp + ws.header);
+    int *tile_start = per_seq ? nullptr : (int *)(wsp + ws.tile_start);
+    int *slot_start = per_seq ? nullptr : (int *)(wsp + ws.slot_start);
+    float *part_lse = per_seq ? nullptr : (float *)(wsp + ws.part_lse);
+    uint16_t *part_out = per_seq ? nullptr : (uint16_t *)(wsp + ws.part_out);
     hipStream_t st_ = (hipStream_t)stream;
     const float sl2 = scale * da::kLog2e;
 
@@ -454,16 +520,12 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
                 hkv, t_max, workers, use_mfma ? "mfma" : "valu");
     bool ok = false;
     if (use_mfma) {
-        hipError_t e;
-        if (d == 64)
-            e = dispatch_gqa_mfma<64>(rows, q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
-                                      tile_start, slot_start, part_out, part_lse, workers, st_);
-        else if (d == 128)
-            e = dispatch_gqa_mfma<128>(rows, q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
-                                       tile_start, slot_start, part_out, part_lse, workers, st_);
-        else
-            e = dispatch_gqa_mfma<256>(rows, q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
-                                       tile_start, slot_start, part_out, part_lse, workers, st_);
+        const GqaArgs a{q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
+                        tile_start, slot_start, part_out, part_lse, workers, st_};
+        const GqaGeom g = gqa_geom(d, hkv, rows);
+        const hipError_t e = d == 64 ? dispatch_gqa_mfma<64>(g, a)
+                             : d == 128 ? dispatch_gqa_mfma<128>(g, a)
+                                        : dispatch_gqa_mfma<256>(g, a);
         if (e != hipSuccess) return DA_ERR_HIP;
         ok = true;
     } else if (d == 64)
@@ -476,7 +538,9 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
         ok = dispatch_gqa_valu<256>(rows, q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
                                     tile_start, slot_start, part_out, part_lse, workers, st_);
     if (!ok) return DA_ERR_UNSUPPORTED;
-    if (d == 64)
+    if (per_seq)
+        ;
+    else if (d == 64)
         launch_combine<64>(b, s * hq, workers, hdr, slot_start, part_out, part_lse, out, lse, st_);
     else if (d == 128)
         launch_combine<128>(b, s * hq, workers, hdr, slot_start, part_out, part_lse, out, lse, st_);
@@ -509,20 +573,22 @@ da_status mla_decode_unabsorbed(const uint16_t *q, const uint16_t *k_cache, cons
 {
     da_status st = unabs_check(b, s, h, dqk, dv, t_max, num_workers);
     if (st != DA_OK) return st;
-    if (!q || !k_cache || !v_cache || !seqlens || !out || !lse || !workspace) return DA_ERR_INVALID_ARG;
+    if (!q || !k_cache || !v_cache || !seqlens || !out || !lse) return DA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return DA_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255u) != 0) return DA_ERR_INVALID_ARG;
     if (!std::isfinite(scale) || !(scale > 0.f)) return DA_ERR_INVALID_ARG;
-    const int workers = unabs_workers(b, h, t_max, num_workers);
+    // a null workspace: one worker per sequence (one split), num_workers ignored
+    const bool per_seq = workspace == nullptr;
+    const int workers = per_seq ? b : unabs_workers(b, h, t_max, num_workers);
     const da::WsLayout ws = da::ws_layout(b, s * h, dv, workers);
-    if (workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
+    if (!per_seq && workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
 
     char *wsp = (char *)workspace;
-    auto *hdr = (da::PlanHeader *)(wsp + ws.header);
-    int *tile_start = (int *)(wsp + ws.tile_start);
-    int *slot_start = (int *)(wsp + ws.slot_start);
-    float *part_lse = (float *)(wsp + ws.part_lse);
-    uint16_t *part_out = (uint16_t *)(wsp + ws.part_out);
+    auto *hdr = per_seq ? nullptr : (da::PlanHeader *)(wsp + ws.header);
+    int *tile_start = per_seq ? nullptr : (int *)(wsp + ws.tile_start);
+    int *slot_start = per_seq ? nullptr : (int *)(wsp + ws.slot_start);
+    float *part_lse = per_seq ? nullptr : (float *)(wsp + ws.part_lse);
+    uint16_t *part_out = per_seq ? nullptr : (uint16_t *)(wsp + ws.part_out);
     hipStream_t st_ = (hipStream_t)stream;
     const float sl2 = scale * da::kLog2e;
     hipError_t e;
@@ -539,7 +605,7 @@ da_status mla_decode_unabsorbed(const uint16_t *q, const uint16_t *k_cache, cons
         e = launch_unabs<4>(q, k_cache, v_cache, seqlens, b, s, h, t_max, sl2, out, lse, hdr, tile_start, slot_start,
                             part_out, part_lse, workers, st_);
     if (e != hipSuccess) return DA_ERR_HIP;
-    launch_combine<kUnabsDV>(b, s * h, workers, hdr, slot_start, part_out, part_lse, out, lse, st_);
+    if (!per_seq) launch_combine<kUnabsDV>(b, s * h, workers, hdr, slot_start, part_out, part_lse, out, lse, st_);
     return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

@@ -51,20 +51,36 @@ __global__ void __launch_bounds__(256)
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int kvh = hb * 4 + wave;
-    // the plan as arrays for the combine kernel; every wave derives its own view
-    if (unit == 0 && wave == 0) write_plan(seqlens, B, t_max, kGqaTile, units / head_blocks, hdr, tile_start, slot_start);
+    const int grp = hq / hkv;
+    const int Rr = grp * s;  // real rows of this KV head
+    const int M = s * hq;    // query rows per sequence
+    // Without a workspace (hdr == nullptr) worker w is sequence w and writes its
+    // rows directly; otherwise one wave writes the plan as arrays for the
+    // combine kernel, and every wave derives its own view of it.
+    const bool per_seq = hdr == nullptr;
+    if (!per_seq && unit == 0 && wave == 0)
+        write_plan(seqlens, B, t_max, kGqaTile, units / head_blocks, hdr, tile_start, slot_start);
     if (kvh >= hkv) return;
 
     PlanWalk cur;
-    if (!cur.init(seqlens, B, t_max, kGqaTile, units / head_blocks, worker)) return;
+    if (per_seq ? !cur.init_per_sequence(seqlens, t_max, kGqaTile, worker)
+                : !cur.init(seqlens, B, t_max, kGqaTile, units / head_blocks, worker)) {
+        if (per_seq) {
+            // a sequence with no cache row: its rows are out = 0, lse = -inf
+            for (int i = lane; i < Rr * (D / 8); i += 64) {
+                const int r = i / (D / 8);
+                const int row = (r / grp) * hq + kvh * grp + r % grp;
+                *(u32x4 *)(out + ((size_t)worker * M + row) * D + (i % (D / 8)) * 8) = u32x4{0u, 0u, 0u, 0u};
+            }
+            for (int r = lane; r < Rr; r += 64) lse[(size_t)worker * M + (r / grp) * hq + kvh * grp + r % grp] = -INFINITY;
+        }
+        return;
+    }
     const int tile_lo = cur.tile_lo;
     const int tile_hi = cur.tile_hi;
 
     const int dg = lane % C::LPT;
     const int slot = lane / C::LPT;
-    const int grp = hq / hkv;
-    const int Rr = grp * s;  // real rows of this KV head
-    const int M = s * hq;    // query rows per sequence
     const size_t tok_stride = (size_t)hkv * D;
 
     uint32_t qv[R][4];
@@ -263,21 +279,25 @@ __global__ void __launch_bounds__(256)
 namespace da {
 
 // ----------------------------------------------------------------------------
-// MFMA kernel (any R = g*s up to 64, rows padded to blocks of 16).
+// MFMA kernel (rows padded to blocks of 16).
 //
-// Block = 512/D... waves (one KV head each); the block streams 16-token stages
-// of its heads' K and V rows HBM -> LDS with buffer_load ... lds (a ring of 4
-// stages, 3 in flight while one is computed; rows past the sequence length read
-// as zeros through the buffer bounds). Per wave and stage:
+// Block = HPB KV heads x RG row groups, one wave each (wave w: head w % HPB,
+// row group w / HPB, which holds RBLK 16-row blocks of that head's R = g*s
+// query rows). The block streams 16-token stages of its heads' K and V rows
+// HBM -> LDS with buffer_load ... lds (a ring of NST stages, NST - 1 in flight
+// while one is computed; rows past the sequence length, and the columns of
+// heads past hkv, read as zeros through the buffer bounds and cost no memory
+// traffic). Every row group of a head reads the same stage from LDS, so the
+// K/V bytes leave HBM once whatever R is. Per wave and stage:
 //   S^T[16 tokens, 16 rows] = K . Q^T   MFMA 16x16x32 bf16, K from LDS, Q in registers
 //   softmax (fp32, exp2 domain, lazily moved per-row reference maximum)
 //   O^T[d, 16 rows] += V^T . P^T        MFMA 16x16x16 bf16, V^T through the LDS
 //                                       transposing read, P^T straight from the
 //                                       score registers
-// LDS stage layout: 16 K token rows then 16 V token rows of 1 KB (the block's
-// heads, d contiguous); 16-byte chunk c of token row t is stored at
-// c ^ gqa_swz(t), which keeps the score reads and the transposing reads free of
-// bank conflicts on 64 banks.
+// LDS stage layout: 16 K token rows then 16 V token rows (the block's heads,
+// d contiguous); 16-byte chunk c of token row t is stored at c ^ gqa_swz(t),
+// which keeps the score reads and the transposing reads free of bank
+// conflicts on 64 banks.
 // Waits until at most `later` * LW copies of this wave are outstanding (`later`
 // runs from 0 to MAXL; the counter limit needs constants).
 template <int LW, int MAXL>
@@ -297,14 +317,18 @@ __device__ __forceinline__ void wait_stage_copies(int later)
 // D: width of the query and key rows (the score dot products); DV: width of
 // the value and output rows (D unless the keys carry extra columns, as the
 // un-absorbed MLA form's decoupled rope part does).
-template <int D, int RBLK, int HPB_ = 512 / D, int NST_ = 4, int DV_ = D>
+template <int D, int RBLK, int HPB_ = 512 / D, int NST_ = 4, int DV_ = D, int RG_ = 1>
 struct GqaMfmaCfg {
     static constexpr int DK = D, DV = DV_;
     static_assert((DK == 64 || DK == 128 || DK == 192 || DK == 256) && (DV == 64 || DV == 128 || DV == 256),
                   "head dims");
-    static constexpr int HPB = HPB_;             // KV heads (waves) per block
+    static_assert(RBLK >= 1 && RBLK <= 4, "one to four 16-row blocks per wave");
+    static constexpr int HPB = HPB_;             // KV heads per block
+    static constexpr int RG = RG_;               // row groups (waves) per head
+    static constexpr int NW = HPB * RG;          // waves per block
     static_assert(HPB >= 1 && HPB * DK <= 512 && HPB * DV <= 512, "token rows of the block's heads fit 1 KB");
-    static constexpr int THREADS = 64 * HPB;
+    static_assert(NW <= 16, "at most 1024 threads");
+    static constexpr int THREADS = 64 * NW;
     static constexpr int T = 16;                 // tokens per stage
     static constexpr int ROWK = HPB * DK * 2;    // bytes of one K token row (HPB heads x DK)
     static constexpr int ROWV = HPB * DV * 2;    // bytes of one V token row
@@ -314,8 +338,8 @@ struct GqaMfmaCfg {
     static constexpr int STAGE_BYTES = T * (ROWK + ROWV);
     static constexpr int NST = NST_;             // ring depth (NST - 1 stages in flight)
     static constexpr int LDS_BYTES = NST * STAGE_BYTES;
-    static constexpr int LW = STAGE_BYTES / 1024 / HPB;  // copy instructions per wave per stage
-    static_assert(LW * HPB * 1024 == STAGE_BYTES, "stage splits into whole copies per wave");
+    static constexpr int LW = STAGE_BYTES / 1024 / NW;  // copy instructions per wave per stage
+    static_assert(LW >= 1 && LW * NW * 1024 == STAGE_BYTES, "stage splits into whole copies per wave");
     static_assert((NST - 2) * LW <= 63, "outstanding copies fit the vmcnt counter");
     static constexpr int KS = DK / 32;           // score k-steps
     static constexpr int DB = DV / 16;           // 16-wide output blocks
@@ -333,8 +357,8 @@ __device__ __forceinline__ int gqa_swz(int t)
 }
 
 
-template <int D, int RBLK, int HPB, int NST, int DV = D>
-__global__ void __launch_bounds__(64 * HPB, 1)
+template <int D, int RBLK, int HPB, int NST, int DV = D, int RG = 1>
+__global__ void __launch_bounds__(64 * HPB * RG, 1)
     gqa_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
                     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens, int B, int s, int hq,
                     int hkv, int t_max, float scale_log2, int head_blocks, int units,
@@ -342,7 +366,7 @@ __global__ void __launch_bounds__(64 * HPB, 1)
                     int *__restrict__ slot_start, uint16_t *__restrict__ out, float *__restrict__ lse,
                     uint16_t *__restrict__ part_out, float *__restrict__ part_lse)
 {
-    using C = GqaMfmaCfg<D, RBLK, HPB, NST, DV>;
+    using C = GqaMfmaCfg<D, RBLK, HPB, NST, DV, RG>;
     constexpr int SUB = kGqaTile / C::T;  // stages per planner tile
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     DA_LDS char *lds = (DA_LDS char *)smem;
@@ -351,25 +375,52 @@ __global__ void __launch_bounds__(64 * HPB, 1)
     if (unit >= units) return;
     const int worker = unit / head_blocks;
     const int hb = unit - worker * head_blocks;
-    // the plan as arrays for the combine kernel; every wave derives its own view
-    if (unit == 0 && threadIdx.x < 64)
-        write_plan(seqlens, B, t_max, kGqaTile, units / head_blocks, hdr, tile_start, slot_start);
-    PlanWalk cur;
-    if (!cur.init(seqlens, B, t_max, kGqaTile, units / head_blocks, worker)) return;
-    const int tile_lo = cur.tile_lo;
-    const int tile_hi = cur.tile_hi;
-    const int nst = (tile_hi - tile_lo) * SUB;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int n = lane & 15;
     const int g = lane >> 4;
-    const int kvh = hb * C::HPB + w;
+    const int hw = w % C::HPB;   // head of the block
+    const int rg = w / C::HPB;   // row group of that head
+    const int kvh = hb * C::HPB + hw;
     const bool active = kvh < hkv;
     const int grp = hq / hkv;
     const int R = grp * s;       // query rows of this KV head
     const int M = s * hq;        // query rows per sequence
+    const int rbase = rg * RBLK * 16;  // first row of this wave
+    const bool rows_here = active && rbase < R;
+    auto row_of = [&](int r) {
+        const int i = r / grp;
+        const int j = r - i * grp;
+        return i * hq + kvh * grp + j;
+    };
+
+    // Without a workspace (hdr == nullptr) worker w is sequence w and writes its
+    // rows directly; otherwise one wave writes the plan as arrays for the
+    // combine kernel, and every wave derives its own view of it.
+    const bool per_seq = hdr == nullptr;
+    if (!per_seq && unit == 0 && threadIdx.x < 64)
+        write_plan(seqlens, B, t_max, kGqaTile, units / head_blocks, hdr, tile_start, slot_start);
+    PlanWalk cur;
+    if (per_seq ? !cur.init_per_sequence(seqlens, t_max, kGqaTile, worker)
+                : !cur.init(seqlens, B, t_max, kGqaTile, units / head_blocks, worker)) {
+        if (per_seq && rows_here) {
+            // a sequence with no cache row: its rows are out = 0, lse = -inf
+            for (int i = lane; i < RBLK * 16 * (DV / 8); i += 64) {
+                const int r = rbase + i / (DV / 8);
+                if (r < R)
+                    *(u32x4 *)(out + ((size_t)worker * M + row_of(r)) * DV + (i % (DV / 8)) * 8) =
+                        u32x4{0u, 0u, 0u, 0u};
+            }
+            for (int i = lane; i < RBLK * 16; i += 64)
+                if (rbase + i < R) lse[(size_t)worker * M + row_of(rbase + i)] = -INFINITY;
+        }
+        return;
+    }
+    const int tile_lo = cur.tile_lo;
+    const int tile_hi = cur.tile_hi;
+    const int nst = (tile_hi - tile_lo) * SUB;
     const int tok_k = hkv * D;   // elements of one token's K row (all KV heads)
     const int tok_v = hkv * DV;  // ... and V row
 
@@ -381,7 +432,7 @@ __global__ void __launch_bounds__(64 * HPB, 1)
     const int hsel = (n & 3) >> 1;
     const int tr_base = C::T * C::ROWK + tr_tok * C::ROWV + ((n & 1) << 3);
 
-    // ---- DMA of one stage: 1 KB copies w, w + HPB, ... (the K rows' chunks, then the V rows')
+    // ---- DMA of one stage: 1 KB copies w, w + NW, ... (the K rows' chunks, then the V rows')
     PlanWalk icur = cur;  // the copies' own cursor, ahead of the compute's
     auto stage_pos = [&](int sg, int &bq, int &tok0) {
         const int tt = tile_lo + sg / SUB;
@@ -389,6 +440,7 @@ __global__ void __launch_bounds__(64 * HPB, 1)
         bq = icur.b;
         tok0 = (tt - icur.ts) * kGqaTile + (sg % SUB) * C::T;
     };
+    const int heads_here = min(C::HPB, hkv - hb * C::HPB);  // heads of this block that exist
     auto issue_stage = [&](int sg) {
         int bq, tok0;
         stage_pos(sg, bq, tok0);
@@ -396,17 +448,21 @@ __global__ void __launch_bounds__(64 * HPB, 1)
         DA_LDS char *dst = lds + (sg % C::NST) * C::STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < C::LW; ++i) {
-            const int cp = w + i * C::HPB;  // wave-uniform copy index
+            const int cp = w + i * C::NW;   // wave-uniform copy index
             const int p = cp * 64 + lane;   // 16-byte chunk of the stage
             const bool is_k = cp * 64 < C::KCH;
             const int rch = is_k ? C::ROWK / 16 : C::ROWV / 16;  // chunks per token row
             const int q = is_k ? p : p - C::KCH;
             const int tk = q / rch;                             // token row of the stage
             const int c = (q - tk * rch) ^ gqa_swz(tk);         // logical chunk in that row
+            const int hd = is_k ? D / 8 : DV / 8;               // chunks per head
             const int te = is_k ? tok_k : tok_v;
             const uint16_t *base = (is_k ? kc : vc) + (size_t)bq * t_max * te;
             const u32x4 rsrc = raw_buffer_rsrc(base, (uint32_t)(L * te * 2));
-            const uint32_t off = (uint32_t)(((tok0 + tk) * te + hb * C::HPB * (is_k ? D : DV)) * 2 + c * 16);
+            // a head past hkv reads as zero (out of range: no memory request)
+            const uint32_t off = c < heads_here * hd
+                                     ? (uint32_t)(((tok0 + tk) * te + hb * C::HPB * hd * 8) * 2 + c * 16)
+                                     : 0x80000000u;
             // each K/V byte is read by this wave's block only: a streaming copy
             lds_dma16_stream(rsrc, dst + cp * 1024, off);
         }
@@ -418,17 +474,12 @@ __global__ void __launch_bounds__(64 * HPB, 1)
     int nvis[RBLK];
     int nvis_min = 0;
 
-    auto row_of = [&](int r) {
-        const int i = r / grp;
-        const int j = r - i * grp;
-        return i * hq + kvh * grp + j;
-    };
     auto begin_segment = [&](int bq) {
         const int L = clamp_len(seqlens[bq], t_max);
         int mn = 0x7fffffff;
 #pragma unroll
         for (int rb = 0; rb < RBLK; ++rb) {
-            const int r = rb * 16 + n;
+            const int r = rbase + rb * 16 + n;
             const bool ok = active && r < R;
             nvis[rb] = ok ? L - s + r / grp + 1 : 0;
             mn = min(mn, nvis[rb]);
@@ -447,13 +498,13 @@ __global__ void __launch_bounds__(64 * HPB, 1)
         nvis_min = mn;
         wait_vm_loads_visible();
     };
-    auto end_segment = [&](int bq, int first_tile_of_seq) {
-        if (!active) return;
+    auto end_segment = [&](int bq) {
+        if (!rows_here) return;
         const int nseg = cur.ns;
         const int sl = cur.slot(worker);
 #pragma unroll
         for (int rb = 0; rb < RBLK; ++rb) {
-            const int r = rb * 16 + n;
+            const int r = rbase + rb * 16 + n;
             if (r >= R) continue;
             const int row = row_of(r);
             const float inv = lsum[rb] > 0.f ? 1.f / lsum[rb] : 0.f;
@@ -488,7 +539,7 @@ __global__ void __launch_bounds__(64 * HPB, 1)
     for (int sg = 0; sg < nst; ++sg) {
         const int tt = tile_lo + sg / SUB;
         if (tt >= te_cur) {  // first stage of a new sequence (stage sg % SUB == 0)
-            end_segment(bcur, ts_cur);
+            end_segment(bcur);
             cur.seek(seqlens, tt);
             bcur = cur.b;
             ts_cur = cur.ts;
@@ -502,7 +553,7 @@ __global__ void __launch_bounds__(64 * HPB, 1)
         if (sg + C::NST - 1 < nst) issue_stage(sg + C::NST - 1);
 
         const int tok0 = (tt - ts_cur) * kGqaTile + (sg % SUB) * C::T;
-        if (!active || tok0 >= L) continue;
+        if (!rows_here || tok0 >= L) continue;
         const DA_LDS char *stg = lds + (sg % C::NST) * C::STAGE_BYTES;
 
         // scores
@@ -511,7 +562,7 @@ __global__ void __launch_bounds__(64 * HPB, 1)
         for (int rb = 0; rb < RBLK; ++rb) S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk) {
-            const int c = w * (D / 8) + kk * 4 + g;
+            const int c = hw * (D / 8) + kk * 4 + g;
             const bf16x8 a = *(const DA_LDS bf16x8 *)(stg + qk_base + ((c ^ sq) << 4));
 #pragma unroll
             for (int rb = 0; rb < RBLK; ++rb) S[rb] = mfma16x16x32(a, qB[rb][kk], S[rb]);
@@ -549,7 +600,7 @@ __global__ void __launch_bounds__(64 * HPB, 1)
         // values
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-            const int c = w * (DV / 8) + 2 * db + hsel;
+            const int c = hw * (DV / 8) + 2 * db + hsel;
             const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (DA_LDS i16x4 *)(stg + tr_base + ((c ^ st) << 4)));
 #pragma unroll
@@ -557,7 +608,7 @@ __global__ void __launch_bounds__(64 * HPB, 1)
                 acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pB[rb], acc[rb][db], 0, 0, 0);
         }
     }
-    end_segment(bcur, ts_cur);
+    end_segment(bcur);
 }
 
 }  // namespace da

@@ -140,10 +140,27 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
     const int worker = unit / row_blocks;
     const int rb = unit - worker * row_blocks;
     const int workers = units / row_blocks;
-    // the plan as arrays for the combine kernel; every wave derives its own view
-    if (unit == 0 && threadIdx.x < 64) write_plan(seqlens, B, t_max, C::T, workers, hdr, tile_start, slot_start);
+    const int M = s * h;  // query rows per sequence
+    // Without a workspace (hdr == nullptr) worker w is sequence w and writes its
+    // rows directly; otherwise one wave writes the plan as arrays for the
+    // combine kernel, and every wave derives its own view of it.
+    const bool per_seq = hdr == nullptr;
+    if (!per_seq && unit == 0 && threadIdx.x < 64)
+        write_plan(seqlens, B, t_max, C::T, workers, hdr, tile_start, slot_start);
     PlanWalk plan;
-    if (!plan.init(seqlens, B, t_max, C::T, workers, worker)) return;
+    if (per_seq ? !plan.init_per_sequence(seqlens, t_max, C::T, worker)
+                : !plan.init(seqlens, B, t_max, C::T, workers, worker)) {
+        if (per_seq) {
+            // a sequence with no cache row: its rows are out = 0, lse = -inf
+            const int r0 = rb * C::ROWS;
+            const int nr = min(C::ROWS, M - r0);
+            uint16_t *o = out + ((size_t)worker * M + r0) * K;
+            for (int i = threadIdx.x; i < nr * (K / 8); i += C::THREADS)
+                *(u32x4 *)(o + (size_t)i * 8) = u32x4{0u, 0u, 0u, 0u};
+            for (int i = threadIdx.x; i < nr; i += C::THREADS) lse[(size_t)worker * M + r0 + i] = -INFINITY;
+        }
+        return;
+    }
     const int tile_lo = plan.tile_lo;
     const int ntiles = plan.tile_hi - tile_lo;
 
@@ -152,7 +169,6 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
     const int lane = tid & 63;
     const int n = lane & 15;
     const int g = lane >> 4;
-    const int M = s * h;  // query rows per sequence
 
     DA_LDS char *pbuf = lds + C::PBUF_OFF;
     DA_LDS float *mref_buf = (DA_LDS float *)(lds + C::MREF_OFF);

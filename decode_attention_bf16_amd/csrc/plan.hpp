@@ -228,6 +228,27 @@ struct PlanWalk {
         return true;  // not reached: some sequence holds tile_lo < total
     }
 
+    // The plan without a workspace: worker w is sequence w, whose tiles are
+    // all its own (one segment, written directly, never merged). Tile indices
+    // are local to the sequence. Returns false for an empty sequence.
+    __device__ bool init_per_sequence(const int32_t *__restrict__ seqlens, int t_max, int tile_, int seq)
+    {
+        tmax = t_max;
+        tile = tile_;
+        const int nt = (clamp_len(seqlens[seq], t_max) + tile - 1) / tile;
+        nb = seq + 1;
+        b = seq;
+        total = nt;
+        per = max(1, nt);
+        tile_lo = 0;
+        tile_hi = nt;
+        ts = 0;
+        te = nt;
+        ss = seq;
+        ns = 1;
+        return nt > 0;
+    }
+
     // Moves the cursor forward to the sequence holding tile tt (tt >= ts).
     __device__ __forceinline__ void seek(const int32_t *__restrict__ seqlens, int tt)
     {

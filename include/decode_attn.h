@@ -40,9 +40,19 @@
  *    seqlens on the host. Buffers must stay alive until the stream's work ends.
  *  - Inputs must not alias outputs or the workspace.
  *
+ * Workspace: device memory the caller passes for the split-KV plan and the
+ * per-segment partial results (size from the matching *_workspace_size,
+ * 256-byte aligned, contents on entry irrelevant). A NULL workspace (with
+ * workspace_bytes ignored) is allowed for the three attention calls and
+ * forces one split: every sequence is one worker's, whose blocks write its
+ * rows directly (no partials, no combine launch; num_workers is ignored).
+ * That path is slower when b times the blocks per sequence is small against
+ * the device's compute units.
+ *
  * Errors: a problem the host can see returns a status and queues nothing.
- *  DA_ERR_INVALID_ARG  null pointer, a dimension <= 0, hq % hkv != 0, s > t_max,
- *                      num_workers < 0, a non-finite scale.
+ *  DA_ERR_INVALID_ARG  null tensor pointer, a dimension <= 0, hq % hkv != 0,
+ *                      s > t_max, num_workers < 0, a non-finite scale, a
+ *                      misaligned pointer.
  *  DA_ERR_UNSUPPORTED  a dimension outside the compiled set (see each call).
  *  DA_ERR_WORKSPACE    workspace_bytes below the matching *_workspace_size.
  *  DA_ERR_HIP          a HIP launch error (the HIP error is cleared).
@@ -97,7 +107,8 @@ size_t mla_decode_workspace_size(int b, int s, int h, int k, int p, int t_max, i
  *   lse     [b, s, h]        fp32   natural-log log-sum-exp of the scaled scores
  *   workspace                device memory of at least
  *                            mla_decode_workspace_size(b, s, h, k, p, t_max, num_workers)
- *                            bytes, 256-byte aligned; its contents on entry do not matter.
+ *                            bytes, 256-byte aligned; its contents on entry do not matter;
+ *                            or NULL (one split per sequence, see above).
  * Compiled set: (k, p) in {(512, 64), (256, 64), (128, 64), (64, 16)}, h >= 1,
  * s * h <= 65536, t_max * (k + p) * 2 < 2^31.
  */
@@ -120,10 +131,12 @@ size_t gqa_decode_workspace_size(int b, int s, int hq, int hkv, int d, int t_max
  *   lse     [b, s, hq]         fp32 (natural log)
  * Query head hh reads K/V head hh / (hq / hkv).
  * Compiled set: d in {64, 128, 256}; R = (hq / hkv) * s query rows per K/V
- * head with R <= 64 (R <= 32 for d = 256); t_max * hkv * d * 2 < 2^31.
+ * head with R <= 256 (R <= 128 for d = 256); t_max * hkv * d * 2 < 2^31.
  * `path` selects the kernel: 1 = VALU dot kernel (R <= 16), 2 = MFMA kernel
- * (rows padded to blocks of 16), 0 = automatic (currently the MFMA kernel for
- * every R). Both give the same result up to rounding.
+ * (rows padded to blocks of 16, spread over up to four waves per K/V head
+ * that share its cache reads), 0 = automatic (currently the MFMA kernel for
+ * every R). Both give the same result up to rounding. Workspace as for
+ * mla_decode (NULL allowed).
  */
 da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
                      const int32_t *seqlens, int b, int s, int hq, int hkv, int d, int t_max,
@@ -148,7 +161,7 @@ size_t mla_decode_unabsorbed_workspace_size(int b, int s, int h, int dqk, int dv
  *   scale                       fp32   multiplies q . k
  *   out     [b, s, h, dv]       bf16
  *   lse     [b, s, h]           fp32   natural log
- * Draft mask, ownership, errors and workspace as for mla_decode.
+ * Draft mask, ownership, errors and workspace (NULL allowed) as for mla_decode.
  * Compiled set: (dqk, dv) = (192, 128) (DeepSeek's 128 + 64 rope / 128);
  * s <= 64; t_max * h * dqk * 2 < 2^31.
  */
@@ -195,8 +208,8 @@ size_t mla_decode_split_cache_workspace_size(int b, int s, int h, int o_max, int
  * Draft i sees every old row and the first n - s + i + 1 new rows (the drafts'
  * own rows are the last s of the new part, so n >= s; with n < s the drafts'
  * order across the split is not the un-split one). Compiled set: latent 512,
- * rope 64, head 128; s <= n_max, s <= 64. Workspace, ownership and errors as
- * for mla_decode.
+ * rope 64, head 128; s <= n_max, s <= 64. Ownership and errors as for
+ * mla_decode; the workspace is required (it also holds the intermediates).
  */
 da_status mla_decode_split_cache(const uint16_t *q_nope, const uint16_t *q_rope, const uint16_t *w_k,
                                  const uint16_t *w_v_t, const uint16_t *latent, const int32_t *seqlens_old,

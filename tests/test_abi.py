@@ -92,7 +92,9 @@ def gqa_call(lib, **kw):
     (dict(s=200, t=128), DA_ERR_INVALID_ARG),
     (dict(nw=-3), DA_ERR_INVALID_ARG),
     (dict(q=None), DA_ERR_INVALID_ARG),
-    (dict(ws=None), DA_ERR_INVALID_ARG),
+    (dict(ws=None, b=0), DA_ERR_INVALID_ARG),    # a null workspace is allowed, but checks still apply
+    (dict(ws=None, q=None), DA_ERR_INVALID_ARG),
+    (dict(ws=ctypes.c_void_p(0x100010)), DA_ERR_INVALID_ARG),  # workspace not 256-byte aligned
     (dict(k=96, p=64), DA_ERR_UNSUPPORTED),
     (dict(k=512, p=32), DA_ERR_UNSUPPORTED),
     (dict(scale=float("nan")), DA_ERR_INVALID_ARG),
@@ -106,7 +108,9 @@ def test_mla_rejects(lib, kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(hq=6, hkv=4), DA_ERR_INVALID_ARG),
     (dict(d=96), DA_ERR_UNSUPPORTED),
-    (dict(hq=64, hkv=1, s=2), DA_ERR_UNSUPPORTED),      # 128 rows per KV head
+    (dict(hq=64, hkv=1, s=5), DA_ERR_UNSUPPORTED),      # 320 rows per KV head (at most 256 at d = 128)
+    (dict(hq=64, hkv=2, s=5, d=256), DA_ERR_UNSUPPORTED),  # 160 rows per KV head (at most 128 at d = 256)
+    (dict(ws=None, hq=6, hkv=4), DA_ERR_INVALID_ARG),
     (dict(hq=32, hkv=1, s=1, path=1), DA_ERR_UNSUPPORTED),  # VALU kernel takes at most 16 rows
     (dict(t=1 << 20, hkv=8, d=256), DA_ERR_UNSUPPORTED),   # 32-bit buffer offsets
     (dict(path=7), DA_ERR_INVALID_ARG),

@@ -3,8 +3,8 @@
 Bar (floating point): max |out - out_ref| <= 1e-2 * max |out_ref| over the
 compared rows, and |lse - lse_ref| <= 1e-3 on rows that see at least one
 cache row; rows that see none must be exactly out = 0, lse = -inf.
-Small shapes are compared on every output; the full-size workloads on a
-seeded sample of rows, in the launch configuration the benchmark times.
+Every test compares every output row, the full-size workloads included, in
+the launch configuration the benchmark times.
 The workspace is poisoned (0xFF bytes = NaN) before every call so that a read
 of an unwritten partial shows up.
 """
@@ -57,13 +57,17 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref, what=""):
         assert lerr <= LSE_TOL, "%s: max|dlse| %.3e" % (what, lerr)
 
 
-def run_mla(da, shape, tensors, num_workers=0, rows=None, oracle_mod=None):
+def run_mla(da, shape, tensors, num_workers=0, null_workspace=False):
     ql, qr, c, sl = tensors
     d = dev()
     g = [t.to(d) for t in (ql, qr, c, sl)]
     nbytes = da.mla_decode_workspace_size(shape.b, shape.s, shape.h, shape.k, shape.p, shape.t_max, num_workers)
-    ws = poisoned(nbytes, d)
-    out, lse = da.mla_decode(*g, shape.scale, num_workers=num_workers, workspace=ws)
+    ws = None if null_workspace else poisoned(nbytes, d)
+    # outputs poisoned too: with no workspace every row must be written by the tile kernel itself
+    out = torch.full((shape.b, shape.s, shape.h, shape.k), float("nan"), dtype=torch.bfloat16, device=d)
+    lse = torch.full((shape.b, shape.s, shape.h), float("nan"), dtype=torch.float32, device=d)
+    da.mla_decode(*g, shape.scale, num_workers=num_workers, workspace=ws, out=out, lse=lse,
+                  null_workspace=null_workspace)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()
 
@@ -152,6 +156,26 @@ def test_mla_many_segments_per_row(da, oracle_mod, case):
     compare(out, lse, ref_o, ref_l, "mla many segments %s" % (case,))
 
 
+@pytest.mark.parametrize("case", MLA_SMALL, ids=lambda c: "b%d_s%d_h%d_k%d_t%d" % (c[0], c[1], c[2], c[3], c[5]))
+def test_mla_null_workspace(da, oracle_mod, case):
+    """No workspace: one worker per sequence writes its rows directly (no split, no combine), including
+    out = 0 / lse = -inf for sequences with no cache row."""
+    b, s, h, k, p, t, sl = case
+    shape = mla_shape(b, s, h, k, p, t, seed=100 + b + s + h)
+    tensors = wl.make_mla(shape, seqlens=sl)
+    print("mla null workspace", case, flush=True)
+    out, lse = run_mla(da, shape, tensors, null_workspace=True)
+    ref_o, ref_l = oracle_mod.mla(*tensors, shape.scale)
+    compare(out, lse, ref_o, ref_l, "mla null workspace %s" % (case,))
+
+
+def test_mla_null_workspace_all_empty(da):
+    shape = mla_shape(3, 2, 16, 64, 16, 40, seed=33)
+    out, lse = run_mla(da, shape, wl.make_mla(shape, seqlens=[0, -5, 0]), null_workspace=True)
+    assert torch.all(out.float() == 0)
+    assert torch.all(torch.isneginf(lse))
+
+
 def test_mla_split_counts_agree(da):
     shape = mla_shape(4, 2, 64, 512, 64, 700, seed=7)
     tensors = wl.make_mla(shape, seqlens=[700, 511, 65, 300])
@@ -231,15 +255,15 @@ def test_mla_score_jumps_in_both_token_halves(da, oracle_mod, workers, pos):
     compare(out, lse, ref_o, ref_l, "score jumps %s workers %d" % (pos, workers))
 
 
-# ------------------------------------------------------------------ MLA, full-size workloads, sampled rows
-def full_size_mla(da, oracle_mod, shape, n_rows=192):
+# ------------------------------------------------------------------ MLA, full-size workloads, every row
+def full_size_mla(da, oracle_mod, shape, null_workspace=False):
     tensors = wl.make_mla(shape)
-    print("full-size mla b=%d s=%d t_max=%d" % (shape.b, shape.s, shape.t_max), flush=True)
-    out, lse = run_mla(da, shape, tensors, 0)
-    rows = wl.sample_rows(shape.rows, n_rows, shape.seed).numpy()
-    ref_o, ref_l = oracle_mod.mla(*tensors, shape.scale, rows=rows)
-    compare(out.reshape(-1, shape.k)[rows], lse.reshape(-1)[rows], ref_o, ref_l, "full mla s=%d" % shape.s)
-    assert torch.isfinite(lse).all() or shape.ragged is not None
+    print("full-size mla b=%d s=%d t_max=%d null_workspace=%s" % (shape.b, shape.s, shape.t_max, null_workspace),
+          flush=True)
+    out, lse = run_mla(da, shape, tensors, 0, null_workspace=null_workspace)
+    ref_o, ref_l = oracle_mod.mla(*tensors, shape.scale)
+    compare(out, lse, ref_o, ref_l, "full mla s=%d" % shape.s)
+    assert torch.isfinite(lse).all()
     return tensors, out, lse
 
 
@@ -247,29 +271,36 @@ def test_mla_dsv3_full_size(da, oracle_mod):
     full_size_mla(da, oracle_mod, wl.MLA_DSV3)
 
 
+def test_mla_dsv3_full_size_null_workspace(da, oracle_mod):
+    full_size_mla(da, oracle_mod, wl.MLA_DSV3, null_workspace=True)
+
+
 def test_mla_mtp4_full_size(da, oracle_mod):
     full_size_mla(da, oracle_mod, wl.MLA_MTP4)
 
 
 def test_mla_ragged_full_size(da, oracle_mod):
-    full_size_mla(da, oracle_mod, wl.MLA_RAGGED, n_rows=96)
+    full_size_mla(da, oracle_mod, wl.MLA_RAGGED)
 
 
 def test_mla_s48_full_size(da, oracle_mod):
     """48 drafts at the DeepSeek-V3-like shapes: 96 row blocks per sequence, for which the automatic
     worker count runs the blocks in several waves over the CUs."""
-    full_size_mla(da, oracle_mod, wl.mla_mtp(48), n_rows=128)
+    full_size_mla(da, oracle_mod, wl.mla_mtp(48))
 
 
 # ------------------------------------------------------------------ GQA
-def run_gqa(da, shape, tensors, num_workers=0, path=0):
+def run_gqa(da, shape, tensors, num_workers=0, path=0, null_workspace=False):
     q, k, v, sl = tensors
     d = dev()
     g = [t.to(d) for t in (q, k, v, sl)]
     nbytes = da.gqa_decode_workspace_size(shape.b, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max, num_workers,
                                           path)
-    ws = poisoned(nbytes, d)
-    out, lse = da.gqa_decode(*g, shape.scale, num_workers=num_workers, path=path, workspace=ws)
+    ws = None if null_workspace else poisoned(nbytes, d)
+    out = torch.full((shape.b, shape.s, shape.hq, shape.d), float("nan"), dtype=torch.bfloat16, device=d)
+    lse = torch.full((shape.b, shape.s, shape.hq), float("nan"), dtype=torch.float32, device=d)
+    da.gqa_decode(*g, shape.scale, num_workers=num_workers, path=path, workspace=ws, out=out, lse=lse,
+                  null_workspace=null_workspace)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()
 
@@ -292,6 +323,14 @@ GQA_SMALL = [
     (2, 5, 16, 2, 128, 160, [160, 77]),      # group 8 x 5 drafts = 40 rows: three row blocks
     (1, 3, 48, 4, 64, 90, [90]),             # group 12 x 3 drafts = 36 rows at d = 64
     (2, 6, 32, 4, 128, 120, [120, 5]),       # 48 rows: three full row blocks, L < s in one sequence
+    (2, 1, 64, 1, 128, 200, [200, 77]),      # MQA, 64 rows: one head per block, rows over four waves
+    (2, 1, 128, 1, 128, 150, [150, 3]),      # MQA, 128 rows: four waves of two row blocks
+    (2, 16, 64, 8, 128, 100, [100, 40]),     # group 8 x 16 drafts = 128 rows
+    (1, 4, 64, 1, 128, 90, [90]),            # 256 rows: four waves of four row blocks
+    (2, 2, 48, 1, 64, 120, [120, 2]),        # MQA at d = 64: two head slots per block, one real
+    (2, 4, 32, 1, 256, 100, [100, 64]),      # 128 rows at d = 256: four waves of two row blocks
+    (2, 3, 24, 2, 128, 130, [130, 30]),      # 36 rows, two KV heads (one head per block)
+    (2, 1, 12, 3, 128, 70, [70, 70]),        # three KV heads at d = 128 (not a multiple of four)
 ]
 
 
@@ -311,6 +350,19 @@ def test_gqa_small(da, oracle_mod, case, path, workers):
     out, lse = run_gqa(da, shape, tensors, workers, path)
     ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale)
     compare(out, lse, ref_o, ref_l, "gqa %s path=%d w=%d" % (case, path, workers))
+
+
+@pytest.mark.parametrize("case,path", [(c, p) for c in GQA_SMALL for p in gqa_paths(c)],
+                         ids=lambda x: ("b%d_s%d_hq%d_hkv%d_d%d" % x[:5]) if isinstance(x, tuple) else "path%d" % x)
+def test_gqa_null_workspace(da, oracle_mod, case, path):
+    """No workspace: one worker per sequence writes its rows directly, empty sequences included."""
+    b, s, hq, hkv, d, t, sl = case
+    shape = wl.GQAShape(b=b, s=s, hq=hq, hkv=hkv, d=d, t_max=t, scale=1.0 / math.sqrt(d), seed=200 + hq + d)
+    tensors = wl.make_gqa(shape, seqlens=sl)
+    print("gqa null workspace", case, "path", path, flush=True)
+    out, lse = run_gqa(da, shape, tensors, 0, path, null_workspace=True)
+    ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale)
+    compare(out, lse, ref_o, ref_l, "gqa null workspace %s path=%d" % (case, path))
 
 
 @pytest.mark.parametrize("path", [1, 2])
@@ -335,15 +387,35 @@ def test_gqa_all_sequences_empty(da, path):
     assert torch.all(torch.isneginf(lse))
 
 
-@pytest.mark.parametrize("path", [1, 2])
-def test_gqa_layer_full_size(da, oracle_mod, path):
-    shape = wl.GQA_LAYER
-    tensors = wl.make_gqa(shape)
-    print("full-size gqa path", path, flush=True)
+@pytest.fixture(scope="module")
+def gqa_full_cases(oracle_mod):
+    """The full-size grouped workloads with the oracle's result for every row (computed once)."""
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            shape = wl.WORKLOADS[name]
+            tensors = wl.make_gqa(shape)
+            cache.clear()  # one multi-GiB workload in memory at a time
+            cache[name] = (shape, tensors) + tuple(oracle_mod.gqa(*tensors, shape.scale))
+        return cache[name]
+    return get
+
+
+@pytest.mark.parametrize("name,path", [("gqa_layer", 1), ("gqa_layer", 2), ("gqa_mqa", 0), ("gqa_mha", 1),
+                                       ("gqa_mha", 2)])
+def test_gqa_full_size(da, gqa_full_cases, name, path):
+    """Every row of the full-size grouped workloads: the layer (group 8), MQA and MHA at b=32/8, t=4096."""
+    shape, tensors, ref_o, ref_l = gqa_full_cases(name)
+    print("full-size %s path %d" % (name, path), flush=True)
     out, lse = run_gqa(da, shape, tensors, 0, path)
-    rows = wl.sample_rows(shape.rows, 512, shape.seed).numpy()
-    ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale, rows=rows)
-    compare(out.reshape(-1, shape.d)[rows], lse.reshape(-1)[rows], ref_o, ref_l, "gqa full path=%d" % path)
+    compare(out, lse, ref_o, ref_l, "%s full path=%d" % (name, path))
+
+
+def test_gqa_layer_full_size_null_workspace(da, gqa_full_cases):
+    shape, tensors, ref_o, ref_l = gqa_full_cases("gqa_layer")
+    out, lse = run_gqa(da, shape, tensors, 0, 0, null_workspace=True)
+    compare(out, lse, ref_o, ref_l, "gqa layer full, null workspace")
 
 
 @pytest.mark.parametrize("path", [1, 2])
@@ -402,16 +474,32 @@ UNABS_SMALL = [
 ]
 
 
+@pytest.mark.parametrize("null_ws", [False, True], ids=["ws", "null_ws"])
 @pytest.mark.parametrize("case", UNABS_SMALL, ids=lambda c: "b%d_s%d_h%d_t%d_w%d" % (c[0], c[1], c[2], c[3], c[5]))
-def test_mla_unabsorbed_small(da, oracle_mod, case):
+def test_mla_unabsorbed_small(da, oracle_mod, case, null_ws):
     b, s, h, t, sl, workers = case
     q, k, v, slt = unabsorbed_inputs(b, s, h, t, sl, seed=400 + b + s + h)
     scale = 1.0 / math.sqrt(192)
     d = dev()
-    out, lse = da.mla_decode_unabsorbed(q.to(d), k.to(d), v.to(d), slt.to(d), scale, num_workers=workers)
+    out = torch.full((b, s, h, 128), float("nan"), dtype=torch.bfloat16, device=d)
+    lse = torch.full((b, s, h), float("nan"), dtype=torch.float32, device=d)
+    da.mla_decode_unabsorbed(q.to(d), k.to(d), v.to(d), slt.to(d), scale, num_workers=workers, out=out, lse=lse,
+                             null_workspace=null_ws)
     torch.cuda.synchronize()
     ref_o, ref_l = unabsorbed_reference(oracle_mod, q, k, v, sl, scale)
     compare(out.cpu(), lse.cpu(), ref_o, ref_l, "mla unabsorbed %s" % (case,))
+
+
+def test_mla_unabsorbed_full_heads(da, oracle_mod):
+    """The crossover's geometry (h=128, t=4096, the automatic worker layout) at b=2 and s=4, every row."""
+    b, s, h, t = 2, 4, 128, 4096
+    q, k, v, slt = unabsorbed_inputs(b, s, h, t, [t, t - 1000], seed=450)
+    scale = 1.0 / math.sqrt(192)
+    d = dev()
+    out, lse = da.mla_decode_unabsorbed(q.to(d), k.to(d), v.to(d), slt.to(d), scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = unabsorbed_reference(oracle_mod, q, k, v, [t, t - 1000], scale)
+    compare(out.cpu(), lse.cpu(), ref_o, ref_l, "mla unabsorbed b=2 s=4 h=128 t=4096")
 
 
 def test_mla_unabsorbed_matches_absorbed(da):

@@ -58,7 +58,7 @@ class GQAShape:
         return self.b * self.s * self.hq
 
 
-# The five workloads. Their names say what they are.
+# The workloads. Their names say what they are.
 MLA_TINY = MLAShape(b=1, s=1, h=16, k=64, p=16, t_max=256, scale=1.0 / math.sqrt(48), seed=0)
 GQA_LAYER = GQAShape(b=32, s=1, hq=64, hkv=8, d=128, t_max=4096, scale=1.0 / math.sqrt(128), seed=1)
 MLA_DSV3 = MLAShape(b=32, s=1, h=128, k=512, p=64, t_max=4096, scale=1.0 / math.sqrt(192), seed=2)
@@ -66,6 +66,11 @@ MLA_MTP4 = MLAShape(b=32, s=4, h=128, k=512, p=64, t_max=4096, scale=1.0 / math.
 MLA_RAGGED = MLAShape(b=64, s=1, h=128, k=512, p=64, t_max=32768, scale=1.0 / math.sqrt(192), seed=4,
                       ragged=(1024, 32768))
 MTP_SWEEP = (1, 2, 4, 8, 16, 32)
+# The two ends of the grouped family at the layer's head geometry ("Why MLA and MTP Fight Each Other",
+# introduction table: MQA's intensity is the number of query heads, MHA's exactly one): one KV head
+# shared by all 64 query heads, and 64 KV heads, one per query head (b=8 keeps its cache at 1 GiB).
+GQA_MQA = GQAShape(b=32, s=1, hq=64, hkv=1, d=128, t_max=4096, scale=1.0 / math.sqrt(128), seed=8)
+GQA_MHA = GQAShape(b=8, s=1, hq=64, hkv=64, d=128, t_max=4096, scale=1.0 / math.sqrt(128), seed=9)
 # The grouped geometry of the "MQA, GQA & MLA" lesson ("01 · Concept": 24 query heads in 4 groups of 6,
 # head dimension 256) at that page's full context: its 16 GiB per sequence over 16 caching layers at
 # 4 KiB per token per layer is 262,144 tokens. One sequence, one layer: K and V are 512 MiB each.
@@ -83,6 +88,8 @@ WORKLOADS = {
     "mla_dsv3": MLA_DSV3,
     "mla_mtp4": MLA_MTP4,
     "mla_ragged": MLA_RAGGED,
+    "gqa_mqa": GQA_MQA,
+    "gqa_mha": GQA_MHA,
 }
 
 
