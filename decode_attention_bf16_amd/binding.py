@@ -25,7 +25,7 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dimensions", 3: "work
 EXPORTED = ("da_version", "da_status_string", "mla_decode_workspace_size", "mla_decode",
             "gqa_decode_workspace_size", "gqa_decode", "mla_decode_unabsorbed_workspace_size",
             "mla_decode_unabsorbed", "mla_absorb_queries", "mla_decompress_output",
-            "mla_decode_split_cache_workspace_size", "mla_decode_split_cache")
+            "mla_decode_split_cache_workspace_size", "mla_decode_split_cache", "mla_decode_no_alloc")
 
 
 class DecodeAttentionError(RuntimeError):
@@ -56,6 +56,8 @@ def load_library():
         lib.mla_decode_workspace_size.restype = Z
         lib.mla_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, P]
         lib.mla_decode.restype = I
+        lib.mla_decode_no_alloc.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, I, P]
+        lib.mla_decode_no_alloc.restype = I
         lib.gqa_decode_workspace_size.argtypes = [I] * 8
         lib.gqa_decode_workspace_size.restype = Z
         lib.gqa_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, I, I, P]
@@ -171,6 +173,30 @@ def mla_decode(q_lat, q_rope, cache, seqlens, scale, num_workers=0, out=None, ls
         rc = lib.mla_decode(_ptr(q_lat), _ptr(q_rope), _ptr(cache), _ptr(seqlens), b, s, h, k, p, t_max,
                             float(scale), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), int(num_workers), _stream(dev))
     _check("mla_decode", rc)
+    return out, lse
+
+
+def mla_decode_no_alloc(q_lat, q_rope, cache, seqlens, scale, out, lse, num_workers=0):
+    """mla_decode through the library's allocation-free entry point: the caller passes the outputs
+    (out [b,s,h,k] bf16, lse [b,s,h] fp32) and no workspace (the library's device scratch holds it)."""
+    lib = load_library()
+    _need(q_lat, "q_lat", torch.bfloat16, 4)
+    dev = q_lat.device
+    _need(q_rope, "q_rope", torch.bfloat16, 4, dev)
+    _need(cache, "cache", torch.bfloat16, 3, dev)
+    _need(seqlens, "seqlens", torch.int32, 1, dev)
+    _need(out, "out", torch.bfloat16, 4, dev)
+    _need(lse, "lse", torch.float32, 3, dev)
+    b, s, h, k = q_lat.shape
+    p = q_rope.shape[3]
+    t_max = cache.shape[1]
+    if (tuple(q_rope.shape) != (b, s, h, p) or tuple(cache.shape) != (b, t_max, k + p) or seqlens.shape[0] != b
+            or tuple(out.shape) != (b, s, h, k) or tuple(lse.shape) != (b, s, h)):
+        raise ValueError("mla_decode_no_alloc shapes: see mla_decode")
+    with torch.cuda.device(dev):
+        rc = lib.mla_decode_no_alloc(_ptr(q_lat), _ptr(q_rope), _ptr(cache), _ptr(seqlens), b, s, h, k, p, t_max,
+                                     float(scale), _ptr(out), _ptr(lse), int(num_workers), _stream(dev))
+    _check("mla_decode_no_alloc", rc)
     return out, lse
 
 

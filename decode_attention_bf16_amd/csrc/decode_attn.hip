@@ -28,6 +28,31 @@ struct DeviceInfo {
 std::mutex g_mutex;
 DeviceInfo g_dev[kMaxDevices];
 
+// Device scratch of mla_decode_no_alloc (the split-KV plan and the partial
+// results that mla_decode keeps in the caller's workspace). Every device the
+// library runs on holds its own copy until the process ends. In host code the
+// name is only a stand-in: the copy's device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[DA_NO_ALLOC_SCRATCH_BYTES];
+void *g_scratch[kMaxDevices];  // device address of `scratch` per device (guarded by g_mutex)
+
+// The current device's copy of `scratch` (nullptr on a HIP error).
+void *current_scratch()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (g_scratch[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch[dev] = p;
+    }
+    return g_scratch[dev];
+}
+
 int current_cu_count()
 {
     int dev = 0;
@@ -462,6 +487,23 @@ da_status mla_decode(const uint16_t *q_lat, const uint16_t *q_rope, const uint16
     else
         e = launch_mla<64, 16>(q_lat, q_rope, cache, seqlens, b, s, h, t_max, sl2, out_lat, lse, ws, wsp, workers, st_);
     return e == hipSuccess ? DA_OK : DA_ERR_HIP;
+}
+
+da_status mla_decode_no_alloc(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *cache,
+                              const int32_t *seqlens, int b, int s, int h, int k, int p, int t_max, float scale,
+                              uint16_t *out_lat, float *lse, int num_workers, void *stream)
+{
+    const da_status st = mla_check(b, s, h, k, p, t_max, num_workers);
+    if (st != DA_OK) return st;
+    // the plan and partials this call needs must fit the device scratch
+    const size_t need = mla_decode_workspace_size(b, s, h, k, p, t_max, num_workers);
+    if (need > (size_t)DA_NO_ALLOC_SCRATCH_BYTES) return DA_ERR_WORKSPACE;
+    void *ws = current_scratch();
+    if (ws == nullptr) return DA_ERR_HIP;
+    // nothing in the scratch has to start at zero: the tile kernel writes the
+    // plan on every call and the combine reads only the slots that plan lists
+    return mla_decode(q_lat, q_rope, cache, seqlens, b, s, h, k, p, t_max, scale, out_lat, lse, ws,
+                      (size_t)DA_NO_ALLOC_SCRATCH_BYTES, num_workers, stream);
 }
 
 static da_status gqa_check(int b, int s, int hq, int hkv, int d, int t_max, int num_workers, int path)

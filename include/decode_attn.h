@@ -117,6 +117,25 @@ da_status mla_decode(const uint16_t *q_lat, const uint16_t *q_rope, const uint16
                      float scale, uint16_t *out_lat, float *lse, void *workspace,
                      size_t workspace_bytes, int num_workers, void *stream);
 
+/*
+ * mla_decode without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). Same arguments,
+ * semantics and errors as mla_decode, minus the workspace: the plan and the
+ * split-KV partials live in a device array inside the library of
+ * DA_NO_ALLOC_SCRATCH_BYTES bytes per device, held until the process ends.
+ * Returns DA_ERR_WORKSPACE when the call needs more than that (the
+ * mla_decode_workspace_size of the same arguments is the need; about 21 MB at
+ * b=32, s=1, h=128, k=512, t=4096 and 34 MB at s=4), DA_ERR_HIP if the
+ * array's device address cannot be obtained. Every call on one device shares
+ * that device's array: calls that overlap on one device (different streams
+ * or host threads without ordering) race and must not be issued.
+ */
+#define DA_NO_ALLOC_SCRATCH_BYTES (64u << 20)
+da_status mla_decode_no_alloc(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *cache,
+                              const int32_t *seqlens, int b, int s, int h, int k, int p, int t_max,
+                              float scale, uint16_t *out_lat, float *lse, int num_workers, void *stream);
+
 /* Bytes of workspace gqa_decode needs for these shapes, num_workers and path
  * (0 for arguments gqa_decode would reject). */
 size_t gqa_decode_workspace_size(int b, int s, int hq, int hkv, int d, int t_max, int num_workers, int path);
