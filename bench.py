@@ -4,27 +4,47 @@
 One step = one pass of the whole hot path over the b=32, t=4096 decode
 workloads: grouped-query decode (64 query / 8 KV heads, d=128, s=1), absorbed
 MLA decode (h=128, k=512, p=64) at s=1, and at s=4 draft tokens. Each call runs
-the device planner, the tile kernel and the log-sum-exp combine. Inputs are
-seeded synthetic bf16 N(0,1) tensors, resident in HBM before timing; the three
-workloads together stream ~840 MB per step, so no input stays in the 256 MB
-last-level cache between its uses.
+the tile kernel (which also derives the split-KV plan) and the log-sum-exp
+combine. Inputs are seeded synthetic bf16 N(0,1) tensors, resident in HBM
+before timing. Every part rotates over enough copies of its inputs that the
+copies together exceed 512 MB (twice the 256 MB last-level cache), so no call
+finds its inputs cached by the previous call of the same part.
 
 Prints ONE JSON line: value = algorithmic TFLOP/s of the step (closed-form
-FLOPs / wall time per step), plus per-part kernel times from HIP events, the
-roofline placement of the dominant call and the fp64 CPU oracle timed on a
-sample of the same rows.
+FLOPs / wall time per step over the K timed steps), plus
+  parts      per-call times from HIP events over the timed steps;
+  timing     per part, the median per-launch time of 5 batches of 20 launches,
+             with and without input rotation;
+  roofline   the dominant call placed on the MI355X roofline, with `traffic`
+             = HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+             of this same invocation (child processes, before this process
+             touches the GPU), scaled by what the counters read for a 1 GiB
+             device copy;
+  parity     every output row of every part against the fp64 oracle;
+  sweep      the MLA s-sweep s = 1..32 and where it crosses the ridge;
+  ragged     the ragged long-context MLA workload (b=64, lengths U{1024..32768});
+  variants   MQA (hkv = 1) and MHA (hkv = hq) at d=128, t=4096, with their
+             measured arithmetic intensity against the closed forms;
+  cpu_baseline the fp64 oracle timed on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--cpu-sample F] [--no-cpu]
-    python bench.py --sweep          # s-sweep of MLA (one JSON line per s, for the ridge crossing)
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-traffic] [--no-extras]
+    python bench.py --crossover | --split | --projections | --gqa-long   (separate studies)
 """
 from __future__ import annotations
 
 import argparse
-import math
+import csv
+import glob
 import hashlib
 import json
+import math
 import os
+import re
+import shutil
+import statistics
+import subprocess
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +60,11 @@ PEAK_TFLOPS = cm.MI355X_BF16_FLOPS / 1e12
 PEAK_GBS = cm.MI355X_HBM_BYTES_PER_S / 1e9
 RIDGE = cm.MI355X_BF16_FLOPS / cm.MI355X_HBM_BYTES_PER_S
 CSRC = os.path.join(ROOT, "decode_attention_bf16_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+ROTATE_BYTES = 512 << 20   # rotation copies of a part's inputs together exceed this
+BATCHES, LAUNCHES = 5, 20  # the protocol's batches of launches
+CALIB_BYTES = 1 << 30      # device copy that calibrates the HBM counters
+METRIC = "decode-attn TFLOP/s + HBM TB/s (% of MI355X roofline), b=32 t=4096, s=1 and s=4"
+OUT_TOL, LSE_TOL = 1e-2, 1e-3
 
 
 def kernel_source_hash() -> str:
@@ -51,40 +75,66 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-class Part:
-    """One decode call of the step, with preallocated outputs and workspace."""
+def _input_bytes(tensors):
+    return sum(t.numel() * t.element_size() for t in tensors)
 
-    def __init__(self, name, kind, shape, dev, path=0):
+
+class Part:
+    """One decode call of the step: `copies` input sets resident on the GPU (set 0 is the seeded
+    workload, the others drawn on the GPU from seeded generators), preallocated outputs and workspace."""
+
+    def __init__(self, name, kind, shape, dev, path=0, copies=None, on_gpu_only=False):
         self.name, self.kind, self.shape, self.path = name, kind, shape, path
         if kind == "mla":
-            cpu = wl.make_mla(shape)
             self.cost = cm.mla_absorbed(shape.b, shape.h, shape.s, shape.t_max, shape.k, shape.p)
-            self.flops_masked = cm.mla_absorbed_ragged(cpu[3].tolist(), shape.h, shape.s, shape.k, shape.p,
-                                                       shape.t_max, masked=True).flops
             nbytes = binding.mla_decode_workspace_size(shape.b, shape.s, shape.h, shape.k, shape.p, shape.t_max)
-            self.out = torch.empty((shape.b, shape.s, shape.h, shape.k), dtype=torch.bfloat16, device=dev)
-            self.lse = torch.empty((shape.b, shape.s, shape.h), dtype=torch.float32, device=dev)
+            oshape, lshape = (shape.b, shape.s, shape.h, shape.k), (shape.b, shape.s, shape.h)
         else:
-            cpu = wl.make_gqa(shape)
             self.cost = cm.gqa(shape.b, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max)
-            self.flops_masked = cm.gqa_ragged(cpu[3].tolist(), shape.s, shape.hq, shape.hkv, shape.d, shape.t_max,
-                                              masked=True).flops
             nbytes = binding.gqa_decode_workspace_size(shape.b, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max, 0,
-                                                       self.path)
-            self.out = torch.empty((shape.b, shape.s, shape.hq, shape.d), dtype=torch.bfloat16, device=dev)
-            self.lse = torch.empty((shape.b, shape.s, shape.hq), dtype=torch.float32, device=dev)
-        self.cpu = cpu
-        self.gpu = [t.to(dev) for t in cpu]
+                                                       path)
+            oshape, lshape = (shape.b, shape.s, shape.hq, shape.d), (shape.b, shape.s, shape.hq)
+        if on_gpu_only:
+            self.cpu = None
+            first = self._draw(dev, 0)
+        else:
+            self.cpu = wl.make_mla(shape) if kind == "mla" else wl.make_gqa(shape)
+            first = tuple(t.to(dev) for t in self.cpu)
+        if shape.ragged is not None:
+            sl = (self.cpu[3] if self.cpu is not None else first[3].cpu()).tolist()
+            self.cost = (cm.mla_absorbed_ragged(sl, shape.h, shape.s, shape.k, shape.p, shape.t_max)
+                         if kind == "mla" else cm.gqa_ragged(sl, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max))
+        n = copies if copies is not None else max(1, math.ceil(ROTATE_BYTES / _input_bytes(first[:3])))
+        self.inputs = [first] + [self._draw(dev, i) for i in range(1, n)]
+        self.out = torch.empty(oshape, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(lshape, dtype=torch.float32, device=dev)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         self.bound = "mfma" if self.cost.ai > RIDGE else "hbm"
         self.t_min = cm.roofline_time(self.cost)
 
-    def __call__(self):
+    def _draw(self, dev, i):
+        """Input set i drawn on the GPU: same shapes, N(0,1) bf16, the workload's lengths."""
+        g = torch.Generator(device=dev).manual_seed(7919 * (i + 1) + self.shape.seed)
+        sh = self.shape
+        r = lambda *s: torch.randn(s, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)  # noqa: E731
+        if self.cpu is not None:
+            sl = self.cpu[3].to(dev)
+        else:  # full-length sequences (every workload drawn only on the GPU is one)
+            sl = torch.full((sh.b,), sh.t_max, dtype=torch.int32, device=dev)
         if self.kind == "mla":
-            binding.mla_decode(*self.gpu, self.shape.scale, out=self.out, lse=self.lse, workspace=self.ws)
+            return (r(sh.b, sh.s, sh.h, sh.k), r(sh.b, sh.s, sh.h, sh.p), r(sh.b, sh.t_max, sh.k + sh.p), sl)
+        return (r(sh.b, sh.s, sh.hq, sh.d), r(sh.b, sh.t_max, sh.hkv, sh.d), r(sh.b, sh.t_max, sh.hkv, sh.d), sl)
+
+    @property
+    def copies(self):
+        return len(self.inputs)
+
+    def __call__(self, i=0):
+        x = self.inputs[i % len(self.inputs)]
+        if self.kind == "mla":
+            binding.mla_decode(*x, self.shape.scale, out=self.out, lse=self.lse, workspace=self.ws)
         else:
-            binding.gqa_decode(*self.gpu, self.shape.scale, path=self.path, out=self.out, lse=self.lse,
-                               workspace=self.ws)
+            binding.gqa_decode(*x, self.shape.scale, path=self.path, out=self.out, lse=self.lse, workspace=self.ws)
 
     def roofline(self, sec):
         if self.bound == "mfma":
@@ -94,104 +144,58 @@ class Part:
         a = self.cost.bytes / sec / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_GBS, "unit": "GB/s", "frac": round(a / PEAK_GBS, 4)}
 
-
-class UnabsorbedPart:
-    """One un-absorbed (per-head K/V) MLA decode call at the DeepSeek-V3-like shapes with s drafts. The
-    decompressed K [b,t,h,192] and V [b,t,h,128] (10.7 GB at b=32, t=4096) are drawn on the GPU from a
-    seeded generator and shared by every s."""
-
-    kv = None
-
-    def __init__(self, s, dev, b=32, h=128, t=4096):
-        self.name, self.s = "mla_unabsorbed_s%d" % s, s
-        if UnabsorbedPart.kv is None:
-            g = torch.Generator(device=dev).manual_seed(7)
-            UnabsorbedPart.kv = (torch.randn((b, t, h, 192), generator=g, device=dev, dtype=torch.bfloat16),
-                                 torch.randn((b, t, h, 128), generator=g, device=dev, dtype=torch.bfloat16),
-                                 torch.full((b,), t, dtype=torch.int32, device=dev))
-        g = torch.Generator(device=dev).manual_seed(100 + s)
-        self.q = torch.randn((b, s, h, 192), generator=g, device=dev, dtype=torch.bfloat16)
-        self.scale = 1.0 / math.sqrt(192)
-        self.out = torch.empty((b, s, h, 128), dtype=torch.bfloat16, device=dev)
-        self.lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
-        nbytes = binding.mla_decode_unabsorbed_workspace_size(b, s, h, 192, 128, t)
-        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-        self.cost = cm.mla_unabsorbed(b, h, s, t, 128, 64)
-
-    def __call__(self):
-        k, v, sl = UnabsorbedPart.kv
-        binding.mla_decode_unabsorbed(self.q, k, v, sl, self.scale, out=self.out, lse=self.lse, workspace=self.ws)
+    def summary(self, sec):
+        return {"us": round(sec * 1e6, 2), "tflops": round(self.cost.flops / sec / 1e12, 2),
+                "tbs": round(self.cost.bytes / sec / 1e12, 3), "ai": round(self.cost.ai, 1), "bound": self.bound,
+                "t_min_us": round(self.t_min * 1e6, 2), "roofline_frac": round(self.t_min / sec, 4)}
 
 
-class ProjectionPart:
-    """One per-head projection call at the DeepSeek-V3-like shapes (h=128, d=128, k=512): the query
-    absorption or the output decompression for b*s query tokens."""
-
-    def __init__(self, kind, s, dev, b=32, h=128, d=128, k=512):
-        self.name, self.kind = "%s_s%d" % (kind, s), kind
-        g = torch.Generator(device=dev).manual_seed(11 + s)
-        if kind == "absorb":
-            self.a = torch.randn((b, s, h, d), generator=g, device=dev, dtype=torch.bfloat16)
-            self.w = torch.randn((h, k, d), generator=g, device=dev, dtype=torch.bfloat16)
-            self.out = torch.empty((b, s, h, k), dtype=torch.bfloat16, device=dev)
-        else:
-            self.a = torch.randn((b, s, h, k), generator=g, device=dev, dtype=torch.bfloat16)
-            self.w = torch.randn((h, d, k), generator=g, device=dev, dtype=torch.bfloat16)
-            self.out = torch.empty((b, s, h, d), dtype=torch.bfloat16, device=dev)
-        m = b * s
-        self.flops = 2.0 * m * h * d * k
-        self.bytes = 2.0 * (h * d * k + m * h * d + m * h * k)  # weights once, input and output rows
-
-    def __call__(self):
-        if self.kind == "absorb":
-            binding.mla_absorb_queries(self.a, self.w, out=self.out)
-        else:
-            binding.mla_decompress_output(self.a, self.w, out=self.out)
-
-
-class SplitPart:
-    """One split-cache MLA decode call (b=32, h=128, t=4096 = o latent + n decompressed rows, s drafts),
-    inputs drawn on the GPU from a seeded generator."""
-
-    def __init__(self, s, n, dev, b=32, h=128, t=4096):
-        self.name, self.s, self.n = "split_s%d_n%d" % (s, n), s, n
-        o = t - n
-        g = torch.Generator(device=dev).manual_seed(900 + n)
-        r = lambda *shape: torch.randn(shape, generator=g, device=dev, dtype=torch.bfloat16)  # noqa: E731
-        self.args = (r(b, s, h, 128), r(b, s, h, 64), r(h, 512, 128), r(h, 128, 512), r(b, max(o, 1), 576),
-                     torch.full((b,), o, dtype=torch.int32, device=dev), r(b, n, h, 192), r(b, n, h, 128),
-                     torch.full((b,), n, dtype=torch.int32, device=dev))
-        self.scale = 1.0 / math.sqrt(192)
-        self.out = torch.empty((b, s, h, 128), dtype=torch.bfloat16, device=dev)
-        self.lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
-        nbytes = binding.mla_decode_split_cache_workspace_size(b, s, h, max(o, 1), n, 0)
-        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-        self.cost = cm.mla_split_latent(b, h, s, o, n, 128, 512, 64)
-
-    def __call__(self):
-        binding.mla_decode_split_cache(*self.args, self.scale, out=self.out, lse=self.lse, workspace=self.ws)
-
-
-def time_parts(parts, steps, warmup):
+def time_steps(parts, steps, warmup):
+    """W untimed steps, then exactly K timed steps (step k uses input copy k of every part), bracketed by
+    device synchronisation. One HIP event on the library's stream at every boundary between consecutive
+    calls (a pair of events around every call costs ~15 us per step more), so a call's time is the
+    difference of the events either side of it."""
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
+    for k in range(warmup):
         for p in parts:
-            p()
-    torch.cuda.synchronize()
-    evs = {p.name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                    for _ in range(steps)] for p in parts}
+            p(k)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps * len(parts) + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    evs[0].record(stream)
+    i = 0
     for k in range(steps):
         for p in parts:
-            a, b = evs[p.name][k]
-            a.record(stream)
-            p()
-            b.record(stream)
+            p(k)
+            i += 1
+            evs[i].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    per = {p.name: sum(a.elapsed_time(b) for a, b in evs[p.name]) / steps / 1e3 for p in parts}
-    return wall, per
+    per = {p.name: 0.0 for p in parts}
+    i = 0
+    for k in range(steps):
+        for p in parts:
+            per[p.name] += evs[i].elapsed_time(evs[i + 1]) / 1e3
+            i += 1
+    return wall, {n: v / steps for n, v in per.items()}
+
+
+def time_batches(part, rotate=True, batches=BATCHES, launches=LAUNCHES, warmup=3):
+    """Per-launch seconds of `batches` batches of `launches` back-to-back calls (HIP events around each
+    batch), rotating over the part's input copies or repeating copy 0. Returns (median, all)."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        part(i if rotate else 0)
+    res = []
+    for bi in range(batches):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(launches):
+            part(bi * launches + i if rotate else 0)
+        b.record(stream)
+        b.synchronize()
+        res.append(a.elapsed_time(b) / 1e3 / launches)
+    return statistics.median(res), res
 
 
 def measured_ceilings(dev, reps=20):
@@ -221,119 +225,279 @@ def measured_ceilings(dev, reps=20):
     return res["copy"], res["gemm"]
 
 
-def ridge_summary(us, dev):
-    """Where the MLA s-sweep crosses the ridge: analytic s* at the published ceilings, at the ceilings
-    measured here, and at this kernel's own best matrix rate; plus the time of each s relative to s=1
-    (flat below the crossing, proportional to s above it)."""
-    sh = wl.mla_mtp(1)
-    bw, fl = measured_ceilings(dev)
-    best = max(tf for _, tf in us.values()) * 1e12
-    cross = lambda f, b: round(cm.mla_ridge_crossing_s(sh.h, sh.k, sh.p, sh.t_max, peak_flops=f, bw=b), 3)
-    return {"sweep_summary": "mla_mtp ridge crossing (b=32, h=128, k=512, p=64, t=4096)",
-            "spec_ridge_flop_per_byte": round(RIDGE, 1),
-            "spec_crossing_s": cross(cm.MI355X_BF16_FLOPS, cm.MI355X_HBM_BYTES_PER_S),
-            "measured_copy_tbs": round(bw / 1e12, 3), "measured_gemm_tflops": round(fl / 1e12, 1),
-            "measured_ridge_flop_per_byte": round(fl / bw, 1), "measured_crossing_s": cross(fl, bw),
-            "kernel_best_tflops": round(best / 1e12, 1), "kernel_crossing_s": cross(best, bw),
-            "time_vs_s1": {str(s): round(t / us[1][0], 3) for s, (t, _) in sorted(us.items())}}
-
-
-def cpu_baseline(parts, fraction):
+# ------------------------------------------------------------------ parity and the CPU baseline
+def oracle_of(part):
+    """The fp64 oracle's result for every row of the part's seeded workload (input copy 0), and the
+    oracle's wall time and multiply-add count."""
     import oracle
     oracle.build(force=False)
-    tot_flops = 0.0
     t0 = time.perf_counter()
-    for p in parts:
-        n = max(1, int(p.shape.rows * fraction))
-        rows = wl.sample_rows(p.shape.rows, n, p.shape.seed).numpy()
-        if p.kind == "mla":
-            _, _, macs = oracle.mla(*p.cpu, p.shape.scale, rows=rows, return_macs=True)
-        else:
-            _, _, macs = oracle.gqa(*p.cpu, p.shape.scale, rows=rows, return_macs=True)
-        tot_flops += 2.0 * macs
-    dt = time.perf_counter() - t0
-    return {"value": round(tot_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "fp64 oracle on a seeded %.0f%% sample of the query rows of each of the step's three "
-                      "workloads (%.1f GFLOP, %.1f s)" % (100 * fraction, tot_flops / 1e9, dt)}
+    fn = oracle.mla if part.kind == "mla" else oracle.gqa
+    o, l, macs = fn(*part.cpu, part.shape.scale, return_macs=True)
+    return o, l, macs, time.perf_counter() - t0
 
 
-def load_traffic(name):
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    ent = t.get(name)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
-        return None
-    return ent.get("bytes_per_call")
+def parity_of(part, ref_o, ref_l):
+    """max |out - out_ref| / max |out_ref| and max |lse - lse_ref| over every row (copy 0's outputs)."""
+    import numpy as np
+    part(0)
+    torch.cuda.synchronize()
+    o = part.out.float().cpu().numpy().astype(np.float64).reshape(ref_o.shape)
+    l = part.lse.cpu().numpy().astype(np.float64).reshape(ref_l.shape)
+    full = ~np.isneginf(ref_l)
+    dout = float(np.abs(o[full] - ref_o[full]).max() / np.abs(ref_o[full]).max()) if full.any() else 0.0
+    dlse = float(np.abs(l[full] - ref_l[full]).max()) if full.any() else 0.0
+    empty_ok = bool(np.all(np.isneginf(l[~full])) and np.all(o[~full] == 0))
+    return {"rows": int(ref_l.size), "max_dout_rel": float("%.3e" % dout), "max_dlse": float("%.3e" % dlse),
+            "pass": bool(dout <= OUT_TOL and dlse <= LSE_TOL and empty_ok and np.isfinite(o).all())}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-sample", type=float, default=1.0,
-                    help="fraction of each workload's query rows the fp64 oracle baseline computes")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--sweep", action="store_true", help="s-sweep of MLA (one JSON line per s)")
-    ap.add_argument("--ragged", action="store_true", help="only the ragged long-context MLA workload")
-    ap.add_argument("--crossover", action="store_true",
-                    help="absorbed vs un-absorbed MLA decode over the s-sweep (b=32, h=128, t=4096)")
-    ap.add_argument("--split", action="store_true",
-                    help="split latent/decompressed cache at s=16 over n (b=32, h=128, t=4096)")
-    ap.add_argument("--projections", action="store_true",
-                    help="per-head query absorption and output decompression (b=32, h=128, d=128, k=512)")
-    ap.add_argument("--gqa-long", action="store_true",
-                    help="only the long-context GQA workload (t=262144, hq=24, hkv=4, d=256), both kernels")
-    ap.add_argument("--only", default="", help="comma list of parts to run (gqa,mla_s1,mla_s4)")
-    ap.add_argument("--gqa-path", type=int, default=0, help="GQA kernel: 0 auto, 1 VALU dot, 2 MFMA")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a plain device-to-device copy of MIB MiB a few times (HBM counter calibration)")
-    args = ap.parse_args()
+# ------------------------------------------------------------------ HBM traffic from the counters
+PROBE_PARTS = ("gqa", "mla_s1", "mla_s4", "gqa_mqa", "gqa_mha")
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (the decode kernels shard by "
-              "batch or KV head with no communication; see DESIGN.md).", file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
+
+def probe_part(name, dev):
+    shapes = {"gqa": ("gqa", wl.GQA_LAYER), "mla_s1": ("mla", wl.MLA_DSV3), "mla_s4": ("mla", wl.MLA_MTP4),
+              "gqa_mqa": ("gqa", wl.GQA_MQA), "gqa_mha": ("gqa", wl.GQA_MHA)}
+    kind, shape = shapes[name]
+    return Part(name, kind, shape, dev, copies=1, on_gpu_only=True)
+
+
+def counter_probe():
+    """Child-process body under rocprofv3: two calls of each probed part in order, then one 1 GiB device
+    copy (the counters' calibration), nothing else on the library's kernels."""
     dev = torch.device("cuda:0")
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
-        return
     binding.load_library()
+    for name in PROBE_PARTS:
+        p = probe_part(name, dev)
+        torch.cuda.synchronize()
+        p(0)
+        p(0)
+        torch.cuda.synchronize()
+        del p
+        torch.cuda.empty_cache()
+    src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe_parts": PROBE_PARTS}), flush=True)
 
-    if args.ragged:
-        p = Part("mla_ragged", "mla", wl.MLA_RAGGED, dev)
-        wall, per = time_parts([p], args.steps, args.warmup)
-        sec = per[p.name]
-        c = cm.mla_absorbed_ragged(p.cpu[3].tolist(), p.shape.h, p.shape.s, p.shape.k, p.shape.p, p.shape.t_max,
-                                   masked=False)
-        t_min = cm.roofline_time(c)
-        print(json.dumps({"workload": "mla_ragged (b=64, s=1, h=128, k=512, p=64, seqlens U{1024..32768}, seed 4)",
-                          "us": round(sec * 1e6, 2), "tflops": round(c.flops / sec / 1e12, 2),
-                          "tbs": round(c.bytes / sec / 1e12, 3), "ai": round(c.ai, 1),
-                          "bound": "mfma" if c.ai > RIDGE else "hbm", "t_min_us": round(t_min * 1e6, 2),
-                          "roofline_frac": round(t_min / sec, 4)}), flush=True)
-        return
 
+def _read_counter_csv(outdir):
+    """[(dispatch id, kernel name, summed counter value)] in dispatch order."""
+    files = glob.glob(os.path.join(outdir, "**", "*counter_collection.csv"), recursive=True)
+    rows = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                did = int(r.get("Dispatch_Id") or r.get("Dispatch_ID") or 0)
+                name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+                val = float(r.get("Counter_Value") or 0.0)
+                ent = rows.setdefault(did, [name, 0.0])
+                ent[1] += val
+    return [(d, n, v) for d, (n, v) in sorted(rows.items())]
+
+
+def measure_traffic():
+    """HBM bytes per call of each probed part, from one FETCH_SIZE run and one WRITE_SIZE run of the counter
+    probe, each scaled by what the same counter reads for the 1 GiB copy. Runs before this process uses
+    the GPU. Returns (dict or None, note)."""
+    prof = shutil.which("rocprofv3")
+    if prof is None:
+        return None, "rocprofv3 not found"
+    env = dict(os.environ, TMPDIR="/tmp")
+    per = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        outdir = tempfile.mkdtemp(prefix="da_pmc_", dir="/tmp")
+        cmd = [prof, "--pmc", ctr, "--output-format", "csv", "-d", outdir, "-o", "pmc", "--", sys.executable,
+               os.path.abspath(__file__), "--counter-probe"]
+        try:
+            r = subprocess.run(cmd, cwd="/tmp", env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                               timeout=240)
+        except subprocess.TimeoutExpired:
+            return None, "%s run timed out" % ctr
+        disp = _read_counter_csv(outdir)
+        shutil.rmtree(outdir, ignore_errors=True)
+        if r.returncode != 0 and not disp:
+            return None, "%s run failed (rc %d): %s" % (ctr, r.returncode, r.stdout.decode()[-300:])
+        mine = lambda n: re.search(r"(^|[^A-Za-z0-9_:])da::", n) is not None  # noqa: E731 (not cuda::)
+        lib = [(n, v) for _, n, v in disp if mine(n)]
+        calib = [v for _, n, v in disp if not mine(n)]
+        if not lib or not calib or calib[-1] <= 0:
+            return None, "%s: no library or calibration dispatches in the counter output" % ctr
+        scale = CALIB_BYTES / (calib[-1] * 1024.0)  # the copy reads (writes) exactly CALIB_BYTES
+        calls = []  # each call: a tile kernel and the combine kernel that follows it
+        for n, v in lib:
+            if "combine" in n and calls:
+                calls[-1] += v
+            else:
+                calls.append(v)
+        if len(calls) != 2 * len(PROBE_PARTS):
+            return None, "%s: %d library calls in the counter output, expected %d" % (ctr, len(calls),
+                                                                                    2 * len(PROBE_PARTS))
+        for i, name in enumerate(PROBE_PARTS):
+            kib = 0.5 * (calls[2 * i] + calls[2 * i + 1])
+            per.setdefault(name, {})[ctr] = {"kib_per_call": round(kib, 1), "scale": round(scale, 4),
+                                              "bytes_per_call": kib * 1024.0 * scale}
+    res = {}
+    for name, d in per.items():
+        res[name] = {"bytes_per_call": round(d["FETCH_SIZE"]["bytes_per_call"] + d["WRITE_SIZE"]["bytes_per_call"]),
+                     "fetch_kib": d["FETCH_SIZE"]["kib_per_call"], "fetch_scale": d["FETCH_SIZE"]["scale"],
+                     "write_kib": d["WRITE_SIZE"]["kib_per_call"], "write_scale": d["WRITE_SIZE"]["scale"]}
+    return res, "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, over two calls per part (mean), scaled by the counters' " \
+                "reading for a 1 GiB device copy"
+
+
+# ------------------------------------------------------------------ the extra keys of the default line
+def sweep_key(dev):
+    """MLA s-sweep at the DeepSeek-V3-like shapes with rotating inputs, and the ridge crossing."""
+    rows, us = [], {}
+    for s in wl.MTP_SWEEP:
+        p = Part("mla_s%d" % s, "mla", wl.mla_mtp(s), dev, on_gpu_only=True)
+        sec, _ = time_batches(p)
+        us[s] = (sec * 1e6, p.cost.flops / sec / 1e12)
+        rows.append(dict({"s": s}, **p.summary(sec)))
+        del p
+        torch.cuda.empty_cache()
+    bw, fl = measured_ceilings(dev)
+    sh = wl.mla_mtp(1)
+    best = max(tf for _, tf in us.values()) * 1e12
+    cross = lambda f, b: round(cm.mla_ridge_crossing_s(sh.h, sh.k, sh.p, sh.t_max, peak_flops=f, bw=b), 3)  # noqa
+    summary = {"spec_ridge_flop_per_byte": round(RIDGE, 1),
+               "spec_crossing_s": cross(cm.MI355X_BF16_FLOPS, cm.MI355X_HBM_BYTES_PER_S),
+               "measured_copy_tbs": round(bw / 1e12, 3), "measured_gemm_tflops": round(fl / 1e12, 1),
+               "measured_ridge_flop_per_byte": round(fl / bw, 1), "measured_crossing_s": cross(fl, bw),
+               "kernel_best_tflops": round(best / 1e12, 1), "kernel_crossing_s": cross(best, bw),
+               "time_vs_s1": {str(s): round(t / us[1][0], 3) for s, (t, _) in sorted(us.items())}}
+    return {"workload": "mla_mtp (b=32, h=128, k=512, p=64, t=4096, s drafts; rotating inputs, median of %d x %d)"
+                        % (BATCHES, LAUNCHES), "points": rows, "ridge": summary}
+
+
+def ragged_key(dev, want_parity):
+    p = Part("mla_ragged", "mla", wl.MLA_RAGGED, dev, copies=1)
+    sec, _ = time_batches(p, rotate=False)
+    res = {"workload": "mla_ragged (b=64, s=1, h=128, k=512, p=64, seqlens U{1024..32768}, seed 4; "
+                       "1.25 GB read per call, median of %d x %d)" % (BATCHES, LAUNCHES)}
+    res.update(p.summary(sec))
+    if want_parity:
+        o, l, _, _ = oracle_of(p)
+        res["parity"] = parity_of(p, o, l)
+    del p
+    torch.cuda.empty_cache()
+    return res
+
+
+def variants_key(dev, traffic, want_parity):
+    """MQA and MHA at the layer's geometry: time, roofline, and the measured intensity (algorithmic FLOPs
+    over counted HBM bytes) against the closed forms (MQA: hq; MHA: 1)."""
+    res = {}
+    for name, shape, closed in (("gqa_mqa", wl.GQA_MQA, "hq = %d" % wl.GQA_MQA.hq),
+                                ("gqa_mha", wl.GQA_MHA, "1")):
+        p = Part(name, "gqa", shape, dev)
+        sec, _ = time_batches(p)
+        ent = {"workload": "b=%d s=%d hq=%d hkv=%d d=%d t=%d, %d rotating copies"
+                           % (shape.b, shape.s, shape.hq, shape.hkv, shape.d, shape.t_max, p.copies)}
+        ent.update(p.summary(sec))
+        ent["ai_kv_only_closed_form"] = closed
+        if traffic and name in traffic:
+            ent["traffic"] = traffic[name]["bytes_per_call"]
+            ent["measured_ai"] = round(p.cost.flops / traffic[name]["bytes_per_call"], 2)
+        if want_parity:
+            o, l, _, _ = oracle_of(p)
+            ent["parity"] = parity_of(p, o, l)
+        res[name] = ent
+        del p
+        torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------ separate studies
+class UnabsorbedPart:
+    """One un-absorbed (per-head K/V) MLA decode call at the DeepSeek-V3-like shapes with s drafts. The
+    decompressed K [b,t,h,192] and V [b,t,h,128] (10.7 GB at b=32, t=4096) are drawn on the GPU from a
+    seeded generator and shared by every s."""
+
+    kv = None
+
+    def __init__(self, s, dev, b=32, h=128, t=4096):
+        self.name, self.s = "mla_unabsorbed_s%d" % s, s
+        if UnabsorbedPart.kv is None:
+            g = torch.Generator(device=dev).manual_seed(7)
+            UnabsorbedPart.kv = (torch.randn((b, t, h, 192), generator=g, device=dev, dtype=torch.bfloat16),
+                                 torch.randn((b, t, h, 128), generator=g, device=dev, dtype=torch.bfloat16),
+                                 torch.full((b,), t, dtype=torch.int32, device=dev))
+        g = torch.Generator(device=dev).manual_seed(100 + s)
+        self.q = torch.randn((b, s, h, 192), generator=g, device=dev, dtype=torch.bfloat16)
+        self.scale = 1.0 / math.sqrt(192)
+        self.out = torch.empty((b, s, h, 128), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
+        nbytes = binding.mla_decode_unabsorbed_workspace_size(b, s, h, 192, 128, t)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.cost = cm.mla_unabsorbed(b, h, s, t, 128, 64)
+
+    def __call__(self, i=0):
+        k, v, sl = UnabsorbedPart.kv
+        binding.mla_decode_unabsorbed(self.q, k, v, sl, self.scale, out=self.out, lse=self.lse, workspace=self.ws)
+
+
+class ProjectionPart:
+    """One per-head projection call at the DeepSeek-V3-like shapes (h=128, d=128, k=512): the query
+    absorption or the output decompression for b*s query tokens."""
+
+    def __init__(self, kind, s, dev, b=32, h=128, d=128, k=512):
+        self.name, self.kind = "%s_s%d" % (kind, s), kind
+        g = torch.Generator(device=dev).manual_seed(11 + s)
+        if kind == "absorb":
+            self.a = torch.randn((b, s, h, d), generator=g, device=dev, dtype=torch.bfloat16)
+            self.w = torch.randn((h, k, d), generator=g, device=dev, dtype=torch.bfloat16)
+            self.out = torch.empty((b, s, h, k), dtype=torch.bfloat16, device=dev)
+        else:
+            self.a = torch.randn((b, s, h, k), generator=g, device=dev, dtype=torch.bfloat16)
+            self.w = torch.randn((h, d, k), generator=g, device=dev, dtype=torch.bfloat16)
+            self.out = torch.empty((b, s, h, d), dtype=torch.bfloat16, device=dev)
+        m = b * s
+        self.flops = 2.0 * m * h * d * k
+        self.bytes = 2.0 * (h * d * k + m * h * d + m * h * k)  # weights once, input and output rows
+
+    def __call__(self, i=0):
+        if self.kind == "absorb":
+            binding.mla_absorb_queries(self.a, self.w, out=self.out)
+        else:
+            binding.mla_decompress_output(self.a, self.w, out=self.out)
+
+
+class SplitPart:
+    """One split-cache MLA decode call (b=32, h=128, t=4096 = o latent + n decompressed rows, s drafts),
+    inputs drawn on the GPU from a seeded generator."""
+
+    def __init__(self, s, n, dev, b=32, h=128, t=4096):
+        self.name, self.s, self.n = "split_s%d_n%d" % (s, n), s, n
+        o = t - n
+        g = torch.Generator(device=dev).manual_seed(900 + n)
+        r = lambda *shape: torch.randn(shape, generator=g, device=dev, dtype=torch.bfloat16)  # noqa: E731
+        self.args = (r(b, s, h, 128), r(b, s, h, 64), r(h, 512, 128), r(h, 128, 512), r(b, max(o, 1), 576),
+                     torch.full((b,), o, dtype=torch.int32, device=dev), r(b, n, h, 192), r(b, n, h, 128),
+                     torch.full((b,), n, dtype=torch.int32, device=dev))
+        self.scale = 1.0 / math.sqrt(192)
+        self.out = torch.empty((b, s, h, 128), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
+        nbytes = binding.mla_decode_split_cache_workspace_size(b, s, h, max(o, 1), n, 0)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.cost = cm.mla_split_latent(b, h, s, o, n, 128, 512, 64)
+
+    def __call__(self, i=0):
+        binding.mla_decode_split_cache(*self.args, self.scale, out=self.out, lse=self.lse, workspace=self.ws)
+
+
+def studies(args, dev):
     if args.crossover:
         first = None
         for s in wl.MTP_SWEEP + (48, 64):
-            pa = Part("mla_s%d" % s, "mla", wl.mla_mtp(s), dev)
+            pa = Part("mla_s%d" % s, "mla", wl.mla_mtp(s), dev, on_gpu_only=True)
             pu = UnabsorbedPart(s, dev)
-            _, per = time_parts([pa, pu], args.steps, args.warmup)
-            ta, tu = per[pa.name], per[pu.name]
+            ta, _ = time_batches(pa)
+            tu, _ = time_batches(pu, rotate=False)
             if first is None and tu < ta:
                 first = s
             print(json.dumps({"crossover": "mla absorbed vs un-absorbed (b=32, h=128, t=4096, k=512, p=64, d=128)",
@@ -346,18 +510,15 @@ def main():
             del pa, pu
         print(json.dumps({"crossover_s": first, "note": "smallest s of the sweep at which the un-absorbed kernel "
                           "is faster (null: none up to s=64)"}), flush=True)
-        return
-
-    if args.split:
+    elif args.split:
         s = 16
-        pa = Part("absorbed_s%d" % s, "mla", wl.mla_mtp(s), dev)
-        _, per = time_parts([pa], args.steps, args.warmup)
-        print(json.dumps({"split": "absorbed only (n=0)", "s": s, "us": round(per[pa.name] * 1e6, 2)}), flush=True)
+        pa = Part("absorbed_s%d" % s, "mla", wl.mla_mtp(s), dev, on_gpu_only=True)
+        ta, _ = time_batches(pa)
+        print(json.dumps({"split": "absorbed only (n=0)", "s": s, "us": round(ta * 1e6, 2)}), flush=True)
         del pa
         for n in (64, 256, 1024, 2048, 4096):
             p = SplitPart(s, n, dev)
-            _, per = time_parts([p], args.steps, args.warmup)
-            sec = per[p.name]
+            sec, _ = time_batches(p, rotate=False)
             t_min = cm.roofline_time(p.cost)
             print(json.dumps({"split": "latent o + decompressed n (b=32, h=128, t=4096)", "s": s, "o": 4096 - n,
                               "n": n, "us": round(sec * 1e6, 2), "tflops": round(p.cost.flops / sec / 1e12, 2),
@@ -366,14 +527,11 @@ def main():
                   flush=True)
             del p
             torch.cuda.empty_cache()
-        return
-
-    if args.projections:
+    elif args.projections:
         for s in (1, 4, 32):
             for kind in ("absorb", "decompress"):
                 p = ProjectionPart(kind, s, dev)
-                _, per = time_parts([p], args.steps, args.warmup)
-                sec = per[p.name]
+                sec, _ = time_batches(p, rotate=False)
                 t_min = max(p.flops / cm.MI355X_BF16_FLOPS, p.bytes / cm.MI355X_HBM_BYTES_PER_S)
                 print(json.dumps({"projection": kind, "b": 32, "s": s, "h": 128, "d": 128, "k": 512,
                                   "us": round(sec * 1e6, 2), "tflops": round(p.flops / sec / 1e12, 2),
@@ -381,38 +539,61 @@ def main():
                                   "t_min_us": round(t_min * 1e6, 2), "roofline_frac": round(t_min / sec, 4)}),
                       flush=True)
                 del p
-        return
-
-    if args.gqa_long:
+    elif args.gqa_long:
         for path in (2, 1):
-            p = Part("gqa_long", "gqa", wl.GQA_LONG, dev, path=path)
-            wall, per = time_parts([p], args.steps, args.warmup)
-            sec = per[p.name]
-            c = p.cost
-            print(json.dumps({"workload": "gqa_long (b=1, s=1, hq=24, hkv=4, d=256, t=262144, seed 6)",
-                              "kernel": "mfma" if path == 2 else "valu",
-                              "us": round(sec * 1e6, 2), "tflops": round(c.flops / sec / 1e12, 3),
-                              "tbs": round(c.bytes / sec / 1e12, 3), "ai": round(c.ai, 1), "bound": p.bound,
-                              "t_min_us": round(p.t_min * 1e6, 2), "roofline_frac": round(p.t_min / sec, 4)}),
-                  flush=True)
+            p = Part("gqa_long", "gqa", wl.GQA_LONG, dev, path=path, copies=1)
+            sec, _ = time_batches(p, rotate=False)
+            print(json.dumps(dict({"workload": "gqa_long (b=1, s=1, hq=24, hkv=4, d=256, t=262144, seed 6)",
+                                   "kernel": "mfma" if path == 2 else "valu"}, **p.summary(sec))), flush=True)
             del p
-        return
+    elif args.sweep:
+        print(json.dumps(sweep_key(dev)), flush=True)
+    elif args.ragged:
+        print(json.dumps(ragged_key(dev, want_parity=False)), flush=True)
 
-    if args.sweep:
-        us = {}
-        for s in wl.MTP_SWEEP:
-            p = Part("mla_s%d" % s, "mla", wl.mla_mtp(s), dev)
-            wall, per = time_parts([p], args.steps, args.warmup)
-            sec = per[p.name]
-            us[s] = (sec * 1e6, p.cost.flops / sec / 1e12)
-            print(json.dumps({"sweep": "mla_mtp", "s": s, "us": round(sec * 1e6, 2),
-                              "tflops": round(p.cost.flops / sec / 1e12, 2),
-                              "tbs": round(p.cost.bytes / sec / 1e12, 3), "ai": round(p.cost.ai, 1),
-                              "bound": p.bound, "t_min_us": round(p.t_min * 1e6, 2),
-                              "roofline_frac": round(p.t_min / sec, 4)}), flush=True)
-            del p
-            torch.cuda.empty_cache()
-        print(json.dumps(ridge_summary(us, dev)), flush=True)
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle: no cpu_baseline, no parity")
+    ap.add_argument("--no-traffic", action="store_true", help="skip the rocprofv3 counter runs (traffic: null)")
+    ap.add_argument("--no-extras", action="store_true", help="only the step: no sweep, ragged or variants keys")
+    ap.add_argument("--only", default="", help="comma list of step parts to run (gqa,mla_s1,mla_s4)")
+    ap.add_argument("--gqa-path", type=int, default=0, help="GQA kernel: 0 auto, 1 VALU dot, 2 MFMA")
+    ap.add_argument("--counter-probe", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--sweep", action="store_true", help="only the MLA s-sweep key")
+    ap.add_argument("--ragged", action="store_true", help="only the ragged long-context MLA key")
+    ap.add_argument("--crossover", action="store_true",
+                    help="absorbed vs un-absorbed MLA decode over the s-sweep (b=32, h=128, t=4096)")
+    ap.add_argument("--split", action="store_true",
+                    help="split latent/decompressed cache at s=16 over n (b=32, h=128, t=4096)")
+    ap.add_argument("--projections", action="store_true",
+                    help="per-head query absorption and output decompression (b=32, h=128, d=128, k=512)")
+    ap.add_argument("--gqa-long", action="store_true",
+                    help="only the long-context GQA workload (t=262144, hq=24, hkv=4, d=256), both kernels")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (the decode kernels shard by "
+              "batch or KV head with no communication; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    if args.counter_probe:
+        counter_probe()
+        return
+    only_study = args.crossover or args.split or args.projections or args.gqa_long or args.sweep or args.ragged
+    traffic, traffic_note = (None, "not measured (--no-traffic)")
+    if not only_study and not args.no_traffic:
+        # the counter runs happen before this process touches the GPU
+        traffic, traffic_note = measure_traffic()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    binding.load_library()
+    if only_study:
+        studies(args, dev)
         return
 
     parts = [Part("gqa", "gqa", wl.GQA_LAYER, dev, args.gqa_path), Part("mla_s1", "mla", wl.MLA_DSV3, dev),
@@ -420,25 +601,31 @@ def main():
     if args.only:
         keep = set(args.only.split(","))
         parts = [p for p in parts if p.name in keep]
-    wall, per = time_parts(parts, args.steps, args.warmup)
+    # the protocol's batches first: they also bring the GPU to its steady clock before the timed steps
+    timing = {}
+    for p in parts:
+        rot, rot_all = time_batches(p, rotate=True)
+        same, same_all = time_batches(p, rotate=False)
+        timing[p.name] = {"rotating_median_us": round(rot * 1e6, 2), "same_input_median_us": round(same * 1e6, 2),
+                          "rotating_batches_us": [round(x * 1e6, 2) for x in rot_all],
+                          "same_input_batches_us": [round(x * 1e6, 2) for x in same_all]}
+    wall, per = time_steps(parts, args.steps, args.warmup)
 
     flops = sum(p.cost.flops for p in parts)
     byts = sum(p.cost.bytes for p in parts)
     dom = max(parts, key=lambda p: per[p.name])
     roof = dom.roofline(per[dom.name])
-    traffic = load_traffic(dom.name)
-    roof["traffic"] = traffic
-    roof["kernel"] = dom.name
+    roof["traffic"] = traffic[dom.name]["bytes_per_call"] if traffic and dom.name in traffic else None
+    roof["kernel"] = dom.name + " (one call: tile kernel + combine, HIP events between calls over the timed steps)"
     part_info = {}
     for p in parts:
-        sec = per[p.name]
-        part_info[p.name] = {"us": round(sec * 1e6, 2), "tflops": round(p.cost.flops / sec / 1e12, 2),
-                             "tbs": round(p.cost.bytes / sec / 1e12, 3), "ai": round(p.cost.ai, 1),
-                             "bound": p.bound, "t_min_us": round(p.t_min * 1e6, 2),
-                             "roofline_frac": round(p.t_min / sec, 4),
-                             "masked_tflops": round(p.flops_masked / sec / 1e12, 2)}
+        part_info[p.name] = dict(p.summary(per[p.name]), copies=p.copies)
+        if traffic and p.name in traffic:
+            part_info[p.name]["traffic"] = traffic[p.name]["bytes_per_call"]
+            part_info[p.name]["traffic_over_algorithmic"] = round(traffic[p.name]["bytes_per_call"] / p.cost.bytes, 3)
+            part_info[p.name]["measured_ai"] = round(p.cost.flops / traffic[p.name]["bytes_per_call"], 1)
     res = {
-        "metric": "decode-attn TFLOP/s + HBM TB/s (% of MI355X roofline), b=32 t=4096, s=1 and s=4",
+        "metric": METRIC,
         "value": round(flops / wall / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -457,10 +644,31 @@ def main():
         "step_roofline_frac": round(sum(p.t_min for p in parts) / wall, 4),
         "roofline": roof,
         "parts": part_info,
+        "timing": dict(timing, protocol="per-launch time, median of %d batches of %d launches; rotating = each "
+                                        "launch takes the next of the part's input copies (together > 512 MB)"
+                                        % (BATCHES, LAUNCHES)),
+        "traffic_note": traffic_note,
         "kernel_source": kernel_source_hash(),
     }
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(parts, args.cpu_sample)
+        import oracle
+        par, tot_macs, tot_sec = {}, 0, 0.0
+        for p in parts:
+            o, l, macs, sec = oracle_of(p)
+            tot_macs += macs
+            tot_sec += sec
+            par[p.name] = parity_of(p, o, l)
+        res["parity"] = par
+        res["cpu_baseline"] = {"value": round(2.0 * tot_macs / tot_sec / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": "fp64 oracle on every query row of the step's three workloads "
+                                         "(%.1f GFLOP, %.1f s)" % (2.0 * tot_macs / 1e9, tot_sec)}
+    if not args.no_extras:
+        del parts
+        torch.cuda.empty_cache()
+        res["sweep"] = sweep_key(dev)
+        res["ragged"] = ragged_key(dev, want_parity=not args.no_cpu)
+        res["variants"] = variants_key(dev, traffic, want_parity=not args.no_cpu)
     print(json.dumps(res), flush=True)
 
 
