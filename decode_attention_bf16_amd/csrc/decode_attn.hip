@@ -249,8 +249,11 @@ int gqa_workers(int b, int hkv, int d, int rows, int path, int t_max, int reques
         w = 2 * current_cu_count() / gqa_head_blocks(hkv);
     } else {
         const GqaGeom g = gqa_geom(d, hkv, rows);
-        // resident blocks per CU: LDS ring, and two waves per SIMD
-        int per_cu = std::min(163840 / gqa_mfma_lds(d, g), std::max(1, 8 / (g.hpb * g.rg)));
+        // resident blocks per CU: the LDS ring allows several; one per CU
+        // measured fastest for both shapes (default heads per block, and one
+        // head per block with its rows over several waves: MQA at hq = 64,
+        // 512 workers 39.9 us, 256 workers 36.9 us)
+        int per_cu = std::min(163840 / gqa_mfma_lds(d, g), 1);
         if (per_cu < 1) per_cu = 1;
         w = per_cu * current_cu_count() / ((hkv + g.hpb - 1) / g.hpb);
     }
@@ -473,10 +476,16 @@ da_status mla_decode(const uint16_t *q_lat, const uint16_t *q_rope, const uint16
     const int workers = workspace ? mla_workers(b, s, h, t_max, num_workers) : b;
     const da::WsLayout ws = da::ws_layout(b, s * h, k, workers);
     if (workspace && workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
+    // When the library's own choice is one worker per sequence (the batch's row
+    // blocks fill the device, e.g. s = 4 at b = 32, h = 128), full-length
+    // sequences are never split, so the call runs in the per-sequence mode: the
+    // same blocks, no plan arrays and no combine launch (an empty combine still
+    // costs its dispatch, ~4 us).
+    const bool per_seq = !workspace || (num_workers == 0 && workers == b);
 
     const float sl2 = scale * da::kLog2e;
     hipStream_t st_ = (hipStream_t)stream;
-    char *wsp = (char *)workspace;
+    char *wsp = per_seq ? nullptr : (char *)workspace;
     hipError_t e = hipSuccess;
     if (k == 512 && p == 64)
         e = launch_mla<512, 64>(q_lat, q_rope, cache, seqlens, b, s, h, t_max, sl2, out_lat, lse, ws, wsp, workers, st_);

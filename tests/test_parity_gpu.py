@@ -169,6 +169,19 @@ def test_mla_null_workspace(da, oracle_mod, case):
     compare(out, lse, ref_o, ref_l, "mla null workspace %s" % (case,))
 
 
+def test_mla_auto_one_worker_per_sequence(da, oracle_mod):
+    """b=8 sequences of s*h = 2048 rows (32 row blocks each): the automatic worker count is one per
+    sequence, so the library runs the per-sequence mode (no plan arrays, no combine) even with a
+    workspace; ragged, draft-shorter and empty sequences included."""
+    shape = mla_shape(8, 32, 64, 512, 64, 200, seed=41)
+    sl = [200, 0, 31, 32, 33, 150, 1, 199]
+    assert da.mla_decode_workspace_size(8, 32, 64, 512, 64, 200) > 0
+    tensors = wl.make_mla(shape, seqlens=sl)
+    out, lse = run_mla(da, shape, tensors, 0)
+    ref_o, ref_l = oracle_mod.mla(*tensors, shape.scale)
+    compare(out, lse, ref_o, ref_l, "mla one worker per sequence")
+
+
 def test_mla_null_workspace_all_empty(da):
     shape = mla_shape(3, 2, 16, 64, 16, 40, seed=33)
     out, lse = run_mla(da, shape, wl.make_mla(shape, seqlens=[0, -5, 0]), null_workspace=True)
