@@ -441,30 +441,35 @@ __global__ void __launch_bounds__(64 * HPB * RG, 1)
         tok0 = (tt - icur.ts) * kGqaTile + (sg % SUB) * C::T;
     };
     const int heads_here = min(C::HPB, hkv - hb * C::HPB);  // heads of this block that exist
+    // Copy i of a wave is a K copy when the stage's K chunks split evenly over
+    // the waves (then known at compile time: the first KCH / (64 NW) copies),
+    // otherwise when its chunk index falls in the K part.
+    constexpr bool KSPLIT = C::KCH % (64 * C::NW) == 0;
+    constexpr int LWK = KSPLIT ? C::KCH / (64 * C::NW) : 0;
     auto issue_stage = [&](int sg) {
         int bq, tok0;
         stage_pos(sg, bq, tok0);
         const int L = clamp_len(seqlens[bq], t_max);
         DA_LDS char *dst = lds + (sg % C::NST) * C::STAGE_BYTES;
+        const u32x4 rsrc_k = raw_buffer_rsrc(kc + (size_t)bq * t_max * tok_k, (uint32_t)(L * tok_k * 2));
+        const u32x4 rsrc_v = raw_buffer_rsrc(vc + (size_t)bq * t_max * tok_v, (uint32_t)(L * tok_v * 2));
 #pragma unroll
         for (int i = 0; i < C::LW; ++i) {
             const int cp = w + i * C::NW;   // wave-uniform copy index
             const int p = cp * 64 + lane;   // 16-byte chunk of the stage
-            const bool is_k = cp * 64 < C::KCH;
+            const bool is_k = KSPLIT ? i < LWK : cp * 64 < C::KCH;
             const int rch = is_k ? C::ROWK / 16 : C::ROWV / 16;  // chunks per token row
             const int q = is_k ? p : p - C::KCH;
             const int tk = q / rch;                             // token row of the stage
             const int c = (q - tk * rch) ^ gqa_swz(tk);         // logical chunk in that row
             const int hd = is_k ? D / 8 : DV / 8;               // chunks per head
             const int te = is_k ? tok_k : tok_v;
-            const uint16_t *base = (is_k ? kc : vc) + (size_t)bq * t_max * te;
-            const u32x4 rsrc = raw_buffer_rsrc(base, (uint32_t)(L * te * 2));
             // a head past hkv reads as zero (out of range: no memory request)
             const uint32_t off = c < heads_here * hd
                                      ? (uint32_t)(((tok0 + tk) * te + hb * C::HPB * hd * 8) * 2 + c * 16)
                                      : 0x80000000u;
             // each K/V byte is read by this wave's block only: a streaming copy
-            lds_dma16_stream(rsrc, dst + cp * 1024, off);
+            lds_dma16_stream(is_k ? rsrc_k : rsrc_v, dst + cp * 1024, off);
         }
     };
 
