@@ -648,6 +648,7 @@ def main():
                                         "launch takes the next of the part's input copies (together > 512 MB)"
                                         % (BATCHES, LAUNCHES)),
         "traffic_note": traffic_note,
+        "traffic_detail": traffic,
         "kernel_source": kernel_source_hash(),
     }
     if not args.no_cpu:
