@@ -365,6 +365,51 @@ hipError_t dispatch_gqa_mfma(const GqaGeom &g, const GqaArgs &a)
     return hipErrorInvalidValue;  // not reached: gqa_check admits only these shapes
 }
 
+// ---- token-group kernel: one block per (sequence, KV head), no split-KV
+constexpr int kGqaTgWaves = 4, kGqaTgNst = 2;
+
+bool gqa_tg_ok(int d, int rows) { return (d == 128 && rows <= 64) || (d == 256 && rows <= 32); }
+
+template <int D, int RBLK>
+hipError_t launch_gqa_tg(const GqaArgs &a)
+{
+    using C = da::GqaTgCfg<D, RBLK, kGqaTgWaves, kGqaTgNst>;
+    auto kern = da::gqa_tg_kernel<D, RBLK, kGqaTgWaves, kGqaTgNst>;
+    static std::once_flag attr_once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(attr_once, [&] {
+        attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    const int units = a.b * a.hkv;
+    const int grid = (units + 7) / 8 * 8;
+    if (log_plan())
+        fprintf(stderr, "[decode_attn] gqa-token-groups d=%d row blocks=%d blocks=%d waves=%d lds=%d\n", D, RBLK,
+                units, kGqaTgWaves, C::LDS_BYTES);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGqaTgWaves), C::LDS_BYTES, a.stream, a.q, a.k, a.v, a.seqlens,
+                       a.s, a.hq, a.hkv, a.t_max, a.scale_log2, units, a.out, a.lse);
+    return hipSuccess;
+}
+
+hipError_t dispatch_gqa_tg(int d, int rows, const GqaArgs &a)
+{
+    const int nrb = (rows + 15) / 16;
+    if (d == 128) {
+        switch (nrb) {
+        case 1: return launch_gqa_tg<128, 1>(a);
+        case 2: return launch_gqa_tg<128, 2>(a);
+        case 3: return launch_gqa_tg<128, 3>(a);
+        case 4: return launch_gqa_tg<128, 4>(a);
+        }
+    } else if (d == 256) {
+        switch (nrb) {
+        case 1: return launch_gqa_tg<256, 1>(a);
+        case 2: return launch_gqa_tg<256, 2>(a);
+        }
+    }
+    return hipErrorInvalidValue;  // not reached: gqa_tg_ok admits only these shapes
+}
+
 // 0 = VALU dot kernel, 1 = MFMA kernel
 int gqa_choose_path(int rows, int path)
 {
@@ -551,8 +596,12 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
     if (!std::isfinite(scale) || !(scale > 0.f)) return DA_ERR_INVALID_ARG;
     const int rows = (hq / hkv) * s;
     const int use_mfma = gqa_choose_path(rows, path);
-    // a null workspace: one worker per sequence (one split), num_workers ignored
-    const bool per_seq = workspace == nullptr;
+    // a null workspace: one worker per sequence (one split), num_workers ignored.
+    // The token-group kernel takes that mode where its shapes allow, and also
+    // the automatic one when the batch gives every CU a (sequence, KV head).
+    const bool tg = use_mfma && gqa_tg_ok(d, rows) &&
+                    (workspace == nullptr || (num_workers == 0 && (long)b * hkv >= current_cu_count()));
+    const bool per_seq = workspace == nullptr || tg;
     const int workers = per_seq ? b : gqa_workers(b, hkv, d, rows, path, t_max, num_workers);
     const da::WsLayout ws = da::ws_layout(b, s * hq, d, workers);
     if (!per_seq && workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
@@ -574,7 +623,8 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
         const GqaArgs a{q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
                         tile_start, slot_start, part_out, part_lse, workers, st_};
         const GqaGeom g = gqa_geom(d, hkv, rows);
-        const hipError_t e = d == 64 ? dispatch_gqa_mfma<64>(g, a)
+        const hipError_t e = tg ? dispatch_gqa_tg(d, rows, a)
+                             : d == 64 ? dispatch_gqa_mfma<64>(g, a)
                              : d == 128 ? dispatch_gqa_mfma<128>(g, a)
                                         : dispatch_gqa_mfma<256>(g, a);
         if (e != hipSuccess) return DA_ERR_HIP;

@@ -378,6 +378,34 @@ def test_gqa_null_workspace(da, oracle_mod, case, path):
     compare(out, lse, ref_o, ref_l, "gqa null workspace %s path=%d" % (case, path))
 
 
+GQA_TOKEN_GROUPS = [
+    # (b, s, hq, hkv, d, t_max): b * hkv >= 256, so the automatic choice (and the null workspace)
+    # runs one block per (sequence, KV head) whose waves split the tokens and merge in LDS
+    (32, 1, 64, 8, 128, 300),    # the layer's geometry, ragged lengths
+    (16, 3, 256, 16, 128, 90),   # group 16 x 3 drafts = 48 rows: three row blocks
+    (64, 4, 16, 4, 128, 70),     # 16 rows over four drafts
+    (32, 8, 64, 8, 128, 60),     # 64 rows: four row blocks
+    (64, 2, 16, 4, 256, 100),    # d = 256, 8 rows
+    (128, 4, 16, 2, 256, 64),    # d = 256, 32 rows: two row blocks
+]
+
+
+@pytest.mark.parametrize("case", GQA_TOKEN_GROUPS, ids=lambda c: "b%d_s%d_hq%d_hkv%d_d%d_t%d" % c)
+@pytest.mark.parametrize("mode", ["auto", "null_workspace", "split"])
+def test_gqa_token_groups(da, oracle_mod, case, mode):
+    """Lengths 0, 1, stage and tile edges and t_max among the sequences; "split" forces the
+    split-KV kernel (explicit worker count) on the same inputs."""
+    b, s, hq, hkv, d, t = case
+    shape = wl.GQAShape(b=b, s=s, hq=hq, hkv=hkv, d=d, t_max=t, scale=1.0 / math.sqrt(d), seed=400 + b + d)
+    edges = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, t - 1, t]
+    sl = [x for x in edges if x <= t] + seeded_lengths(b, t, 41)
+    tensors = wl.make_gqa(shape, seqlens=sl[:b])
+    print("gqa token groups", case, mode, flush=True)
+    out, lse = run_gqa(da, shape, tensors, 96 if mode == "split" else 0, 2, null_workspace=mode == "null_workspace")
+    ref_o, ref_l = oracle_mod.gqa(*tensors, shape.scale)
+    compare(out, lse, ref_o, ref_l, "gqa token groups %s %s" % (case, mode))
+
+
 @pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("workers", [0, 3])
 def test_gqa_many_sequences(da, oracle_mod, path, workers):
@@ -415,14 +443,17 @@ def gqa_full_cases(oracle_mod):
     return get
 
 
-@pytest.mark.parametrize("name,path", [("gqa_layer", 1), ("gqa_layer", 2), ("gqa_mqa", 0), ("gqa_mha", 1),
-                                       ("gqa_mha", 2)])
-def test_gqa_full_size(da, gqa_full_cases, name, path):
-    """Every row of the full-size grouped workloads: the layer (group 8), MQA and MHA at b=32/8, t=4096."""
+@pytest.mark.parametrize("name,path,workers", [("gqa_layer", 1, 0), ("gqa_layer", 2, 0), ("gqa_layer", 2, 128),
+                                               ("gqa_mqa", 0, 0), ("gqa_mha", 1, 0), ("gqa_mha", 2, 0),
+                                               ("gqa_mha", 2, 64)])
+def test_gqa_full_size(da, gqa_full_cases, name, path, workers):
+    """Every row of the full-size grouped workloads: the layer (group 8), MQA and MHA at b=32/8, t=4096.
+    The automatic worker count runs the layer and MHA one block per (sequence, KV head); an explicit
+    worker count runs the split-KV kernel and the combine."""
     shape, tensors, ref_o, ref_l = gqa_full_cases(name)
-    print("full-size %s path %d" % (name, path), flush=True)
-    out, lse = run_gqa(da, shape, tensors, 0, path)
-    compare(out, lse, ref_o, ref_l, "%s full path=%d" % (name, path))
+    print("full-size %s path %d workers %d" % (name, path, workers), flush=True)
+    out, lse = run_gqa(da, shape, tensors, workers, path)
+    compare(out, lse, ref_o, ref_l, "%s full path=%d workers=%d" % (name, path, workers))
 
 
 def test_gqa_layer_full_size_null_workspace(da, gqa_full_cases):
