@@ -366,15 +366,32 @@ hipError_t dispatch_gqa_mfma(const GqaGeom &g, const GqaArgs &a)
 }
 
 // ---- token-group kernel: one block per (sequence, KV head), no split-KV
-constexpr int kGqaTgWaves = 4, kGqaTgNst = 2;
+constexpr int kGqaTgNst = 2;
 
 bool gqa_tg_ok(int d, int rows) { return (d == 128 && rows <= 64) || (d == 256 && rows <= 32); }
 
-template <int D, int RBLK>
+// Waves per block: about 32 KB of stage copies in flight per CU (one 16-token
+// stage per wave: four waves per CU at d = 128, two at d = 256) measured
+// fastest at every batch shape tried (per call, 0.54 GB of K/V unless noted):
+//   d = 128, b*hkv =  256: 4 waves 82.5 us, 2 waves 100.7, 1 wave 176
+//   d = 128, b*hkv =  512: 2 waves 87-89, 4 waves 91-93 (MHA, 1.07 GB: 165 vs 178)
+//   d = 128, b*hkv = 1024: 1 wave 85-87, 2 waves 92, 4 waves 89
+//   d = 256, b*hkv =  256: 2 waves 82.5-83, 4 waves 83, 1 wave 118
+//   d = 256, b*hkv =  512: 1 wave 82.5, 2 waves 85.5, 4 waves 86.5
+int gqa_tg_waves(int units, int d)
+{
+    const int per_cu = d == 128 ? 4 : 2;  // waves per CU for ~32 KB in flight
+    const long budget = 3L * per_cu * current_cu_count();
+    for (int tg = 4; tg > 1; tg >>= 1)
+        if (2L * tg * units <= budget) return tg;
+    return 1;
+}
+
+template <int D, int RBLK, int TG>
 hipError_t launch_gqa_tg(const GqaArgs &a)
 {
-    using C = da::GqaTgCfg<D, RBLK, kGqaTgWaves, kGqaTgNst>;
-    auto kern = da::gqa_tg_kernel<D, RBLK, kGqaTgWaves, kGqaTgNst>;
+    using C = da::GqaTgCfg<D, RBLK, TG, kGqaTgNst>;
+    auto kern = da::gqa_tg_kernel<D, RBLK, TG, kGqaTgNst>;
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(attr_once, [&] {
@@ -385,26 +402,32 @@ hipError_t launch_gqa_tg(const GqaArgs &a)
     const int grid = (units + 7) / 8 * 8;
     if (log_plan())
         fprintf(stderr, "[decode_attn] gqa-token-groups d=%d row blocks=%d blocks=%d waves=%d lds=%d\n", D, RBLK,
-                units, kGqaTgWaves, C::LDS_BYTES);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGqaTgWaves), C::LDS_BYTES, a.stream, a.q, a.k, a.v, a.seqlens,
-                       a.s, a.hq, a.hkv, a.t_max, a.scale_log2, units, a.out, a.lse);
+                units, TG, C::LDS_BYTES);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * TG), C::LDS_BYTES, a.stream, a.q, a.k, a.v, a.seqlens, a.s, a.hq,
+                       a.hkv, a.t_max, a.scale_log2, units, a.out, a.lse);
     return hipSuccess;
 }
 
-hipError_t dispatch_gqa_tg(int d, int rows, const GqaArgs &a)
+template <int D, int RBLK>
+hipError_t launch_gqa_tg_waves(int tg, const GqaArgs &a)
+{
+    return tg == 4 ? launch_gqa_tg<D, RBLK, 4>(a) : tg == 2 ? launch_gqa_tg<D, RBLK, 2>(a) : launch_gqa_tg<D, RBLK, 1>(a);
+}
+
+hipError_t dispatch_gqa_tg(int d, int rows, int tg, const GqaArgs &a)
 {
     const int nrb = (rows + 15) / 16;
     if (d == 128) {
         switch (nrb) {
-        case 1: return launch_gqa_tg<128, 1>(a);
-        case 2: return launch_gqa_tg<128, 2>(a);
-        case 3: return launch_gqa_tg<128, 3>(a);
-        case 4: return launch_gqa_tg<128, 4>(a);
+        case 1: return launch_gqa_tg_waves<128, 1>(tg, a);
+        case 2: return launch_gqa_tg_waves<128, 2>(tg, a);
+        case 3: return launch_gqa_tg_waves<128, 3>(tg, a);
+        case 4: return launch_gqa_tg_waves<128, 4>(tg, a);
         }
     } else if (d == 256) {
         switch (nrb) {
-        case 1: return launch_gqa_tg<256, 1>(a);
-        case 2: return launch_gqa_tg<256, 2>(a);
+        case 1: return launch_gqa_tg_waves<256, 1>(tg, a);
+        case 2: return launch_gqa_tg_waves<256, 2>(tg, a);
         }
     }
     return hipErrorInvalidValue;  // not reached: gqa_tg_ok admits only these shapes
@@ -623,7 +646,7 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
         const GqaArgs a{q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
                         tile_start, slot_start, part_out, part_lse, workers, st_};
         const GqaGeom g = gqa_geom(d, hkv, rows);
-        const hipError_t e = tg ? dispatch_gqa_tg(d, rows, a)
+        const hipError_t e = tg ? dispatch_gqa_tg(d, rows, gqa_tg_waves(b * hkv, d), a)
                              : d == 64 ? dispatch_gqa_mfma<64>(g, a)
                              : d == 128 ? dispatch_gqa_mfma<128>(g, a)
                                         : dispatch_gqa_mfma<256>(g, a);

@@ -629,10 +629,11 @@ __global__ void __launch_bounds__(64 * HPB * RG, 1)
 // merged per row. The per-stage arithmetic and the LDS layout are those of the
 // MFMA kernel above with one head per block.
 //
-// Ring depth: two stages per wave (one in flight while the other is computed)
-// measured fastest at the layer's geometry (b = 32, hkv = 8, d = 128,
-// t = 4096): four waves per block x two stages 81.4-81.9 us per call against
-// 86.7-88.4 with three stages, 87-88 with eight waves and 101 with two waves.
+// Ring depth: two stages per wave (one in flight while the other is computed).
+// At the layer's geometry (b = 32, hkv = 8, d = 128, t = 4096; four waves per
+// block) that measured 81.4-81.9 us per call against 86.7-88.4 with three
+// stages; more bytes in flight per CU only slowed the stream (the host picks
+// the waves per block for about 32 KB in flight per CU).
 template <int D, int RBLK, int TG, int NST>
 struct GqaTgCfg {
     static_assert(D == 128 || D == 256, "head dim");
