@@ -31,7 +31,7 @@ between calls), plus
   cpu_baseline the fp64 oracle timed on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-traffic] [--no-extras]
-    python bench.py --crossover | --split | --projections | --gqa-long   (separate studies)
+    python bench.py --crossover | --split | --projections | --gqa-long | --cu-scaling   (separate studies)
 """
 from __future__ import annotations
 
@@ -547,6 +547,23 @@ def studies(args, dev):
                   flush=True)
             del p
             torch.cuda.empty_cache()
+    elif args.cu_scaling:
+        # the K/V stream (GQA token-group kernel, 0.54 GB per call) on 32..256 blocks, one per CU
+        for blocks in (32, 64, 128, 256):
+            b = blocks // 8
+            shape = wl.GQAShape(b=b, s=1, hq=64, hkv=8, d=128, t_max=4096 * 32 // b, scale=1.0 / math.sqrt(128),
+                                seed=12)
+            p = Part("gqa_%dblocks" % blocks, "gqa", shape, dev, copies=1, on_gpu_only=True)
+
+            def call(i=0, p=p):
+                binding.gqa_decode(*p.inputs[0], shape.scale, out=p.out, lse=p.lse, null_workspace=True)
+            sec, _ = time_batches(call, rotate=False)
+            print(json.dumps({"cu_scaling": "GQA K/V stream, one block per (sequence, KV head), 0.54 GB per call",
+                              "blocks": blocks, "b": b, "t": shape.t_max, "us": round(sec * 1e6, 2),
+                              "tbs": round(p.cost.bytes / sec / 1e12, 3),
+                              "gbs_per_block": round(p.cost.bytes / sec / 1e9 / blocks, 1)}), flush=True)
+            del p
+            torch.cuda.empty_cache()
     elif args.projections:
         for s in (1, 4, 32):
             for kind in ("absorb", "decompress"):
@@ -591,6 +608,8 @@ def main():
                     help="split latent/decompressed cache at s=16 over n (b=32, h=128, t=4096)")
     ap.add_argument("--projections", action="store_true",
                     help="per-head query absorption and output decompression (b=32, h=128, d=128, k=512)")
+    ap.add_argument("--cu-scaling", action="store_true",
+                    help="HBM rate of the K/V stream on 32..256 blocks (one per CU), 0.54 GB per call")
     ap.add_argument("--gqa-long", action="store_true",
                     help="only the long-context GQA workload (t=262144, hq=24, hkv=4, d=256), both kernels")
     args = ap.parse_args()
@@ -602,7 +621,8 @@ def main():
     if args.counter_probe:
         counter_probe()
         return
-    only_study = args.crossover or args.split or args.projections or args.gqa_long or args.sweep or args.ragged
+    only_study = (args.crossover or args.split or args.projections or args.gqa_long or args.sweep or args.ragged
+                  or args.cu_scaling)
     traffic, traffic_note = (None, "not measured (--no-traffic)")
     if not only_study and not args.no_traffic:
         # the counter runs happen before this process touches the GPU
