@@ -14,8 +14,10 @@ finds its inputs cached by the previous call of the same part.
 Prints ONE JSON line: value = algorithmic TFLOP/s of the step (closed-form
 FLOPs / wall time per step over the K timed steps, which have no marker
 between calls), plus
-  parts      per-call times from HIP events at every call boundary over a
-             second pass of the K steps (each marker adds a dispatch gap);
+  parts      per-call times inside the step: the unmarked K steps minus the
+             unmarked K steps without that call; and from HIP events at
+             every call boundary over another pass (each marker adds a
+             dispatch gap);
   timing     per part, the median per-launch time of 5 batches of 20 launches,
              with and without input rotation;
   roofline   the dominant call placed on the MI355X roofline, with `traffic`
@@ -174,12 +176,36 @@ def time_steps(parts, steps, warmup):
     return wall, a.elapsed_time(b) / 1e3 / steps
 
 
+def time_marginal(parts, steps, reps=3):
+    """Each call's time inside the step without any marker between calls: the K steps timed with HIP events
+    at their two ends only, once with every part and once with each part left out (median of `reps`
+    repetitions of each); a call's time is the difference. Returns {name: seconds}."""
+    stream = torch.cuda.current_stream()
+
+    def run(ps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for p in ps:
+            p(0)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for k in range(steps):
+            for p in ps:
+                p(k)
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / 1e3 / steps
+
+    full = statistics.median(run(parts) for _ in range(reps))
+    return {p.name: full - statistics.median(run([q for q in parts if q is not p]) for _ in range(reps))
+            for p in parts}
+
+
 def time_calls(parts, steps):
-    """Per-call breakdown of the step: the same K steps once more with one HIP event on the library's stream at
-    every boundary between consecutive calls, so a call's time is the difference of the events either side of
-    it. A marker between two calls delays the next dispatch by a few microseconds (the queue waits for the
-    marker's completion), so each call's time here includes one such gap and the calls add up to more than the
-    unmarked step of time_steps."""
+    """Per-call breakdown of the step with markers: the same K steps once more with one HIP event on the
+    library's stream at every boundary between consecutive calls, so a call's time is the difference of
+    the events either side of it. A marker between two calls delays the next dispatch by a few
+    microseconds (the queue waits for the marker's completion), so each call's time here includes one such
+    gap and the calls add up to more than the unmarked step of time_steps."""
     stream = torch.cuda.current_stream()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps * len(parts) + 1)]
     torch.cuda.synchronize()
@@ -649,19 +675,22 @@ def main():
         timing[p.name] = {"rotating_median_us": round(rot * 1e6, 2), "same_input_median_us": round(same * 1e6, 2),
                           "rotating_batches_us": [round(x * 1e6, 2) for x in rot_all],
                           "same_input_batches_us": [round(x * 1e6, 2) for x in same_all]}
+    # per-call breakdowns first (marked pass, then the unmarked differences), then the W warmup and the K
+    # timed steps, which are thus the last calls of the run
+    marked = time_calls(parts, args.steps)
+    per = time_marginal(parts, args.steps) if len(parts) > 1 else marked
     wall, ev_step = time_steps(parts, args.steps, args.warmup)
-    per = time_calls(parts, args.steps)
 
     flops = sum(p.cost.flops for p in parts)
     byts = sum(p.cost.bytes for p in parts)
     dom = max(parts, key=lambda p: per[p.name])
     roof = dom.roofline(per[dom.name])
     roof["traffic"] = traffic[dom.name]["bytes_per_call"] if traffic and dom.name in traffic else None
-    roof["kernel"] = dom.name + (" (one call: HIP events at the call's boundaries over K steps, which include one "
-                                 "marker gap; the call is the tile kernel alone at this shape)")
+    roof["kernel"] = dom.name + (" (one call inside the step: K unmarked steps minus K unmarked steps without "
+                                 "it, HIP events; the call is the tile kernel alone at this shape)")
     part_info = {}
     for p in parts:
-        part_info[p.name] = dict(p.summary(per[p.name]), copies=p.copies)
+        part_info[p.name] = dict(p.summary(per[p.name]), copies=p.copies, marked_us=round(marked[p.name] * 1e6, 2))
         if traffic and p.name in traffic:
             part_info[p.name]["traffic"] = traffic[p.name]["bytes_per_call"]
             part_info[p.name]["traffic_over_algorithmic"] = round(traffic[p.name]["bytes_per_call"] / p.cost.bytes, 3)
@@ -687,8 +716,9 @@ def main():
         "step_roofline_frac": round(sum(p.t_min for p in parts) / wall, 4),
         "roofline": roof,
         "parts": part_info,
-        "parts_note": ("per call: HIP events at every call boundary over a second pass of the K steps; each marker "
-                       "adds a dispatch gap, so these sum to more than ms_per_step"),
+        "parts_note": ("us: a call's time inside the step with no marker between calls (K unmarked steps minus K "
+                       "unmarked steps without that call, medians of 3); marked_us: HIP events at every call "
+                       "boundary over another pass of the K steps, each marker adding a dispatch gap"),
         "timing": dict(timing, protocol="per-launch time, median of %d batches of %d launches; rotating = each "
                                         "launch takes the next of the part's input copies (together > 512 MB)"
                                         % (BATCHES, LAUNCHES)),
