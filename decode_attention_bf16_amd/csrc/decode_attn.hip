@@ -175,6 +175,7 @@ hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint1
 // ------------------------------------------------------------------ GQA
 int gqa_head_blocks(int hkv) { return (hkv + 3) / 4; }
 int gqa_choose_path(int rows, int path);
+bool gqa_tg_ok(int d, int rows);
 
 // Launch shape of the MFMA kernel: KV heads per block, row-group waves per
 // head and 16-row blocks per wave. The default block holds kBase heads with
@@ -245,7 +246,10 @@ int gqa_workers(int b, int hkv, int d, int rows, int path, int t_max, int reques
 {
     if (requested > 0) return requested;
     int w;
-    if (gqa_choose_path(rows, path) == 0) {
+    if (gqa_choose_path(rows, path) == 1 && gqa_tg_ok(d, rows)) {
+        // token-group kernel: one block (worker, KV head) per CU
+        w = current_cu_count() / hkv;
+    } else if (gqa_choose_path(rows, path) == 0) {
         w = 2 * current_cu_count() / gqa_head_blocks(hkv);
     } else {
         const GqaGeom g = gqa_geom(d, hkv, rows);
@@ -398,13 +402,14 @@ hipError_t launch_gqa_tg(const GqaArgs &a)
         attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     });
     if (attr_err != hipSuccess) return attr_err;
-    const int units = a.b * a.hkv;
+    const int units = a.workers * a.hkv;
     const int grid = (units + 7) / 8 * 8;
     if (log_plan())
-        fprintf(stderr, "[decode_attn] gqa-token-groups d=%d row blocks=%d blocks=%d waves=%d lds=%d\n", D, RBLK,
-                units, TG, C::LDS_BYTES);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * TG), C::LDS_BYTES, a.stream, a.q, a.k, a.v, a.seqlens, a.s, a.hq,
-                       a.hkv, a.t_max, a.scale_log2, units, a.out, a.lse);
+        fprintf(stderr, "[decode_attn] gqa-token-groups d=%d row blocks=%d workers=%d blocks=%d waves=%d lds=%d\n", D,
+                RBLK, a.workers, units, TG, C::LDS_BYTES);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * TG), C::LDS_BYTES, a.stream, a.q, a.k, a.v, a.seqlens, a.b, a.s,
+                       a.hq, a.hkv, a.t_max, a.scale_log2, units, a.hdr, a.tile_start, a.slot_start, a.out, a.lse,
+                       a.part_out, a.part_lse);
     return hipSuccess;
 }
 
@@ -622,9 +627,9 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
     // a null workspace: one worker per sequence (one split), num_workers ignored.
     // The token-group kernel takes that mode where its shapes allow, and also
     // the automatic one when the batch gives every CU a (sequence, KV head).
-    const bool tg = use_mfma && gqa_tg_ok(d, rows) &&
-                    (workspace == nullptr || (num_workers == 0 && (long)b * hkv >= current_cu_count()));
-    const bool per_seq = workspace == nullptr || tg;
+    const bool tg = use_mfma && gqa_tg_ok(d, rows);
+    const bool per_seq =
+        workspace == nullptr || (tg && num_workers == 0 && (long)b * hkv >= current_cu_count());
     const int workers = per_seq ? b : gqa_workers(b, hkv, d, rows, path, t_max, num_workers);
     const da::WsLayout ws = da::ws_layout(b, s * hq, d, workers);
     if (!per_seq && workspace_bytes < ws.total) return DA_ERR_WORKSPACE;
@@ -646,7 +651,7 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
         const GqaArgs a{q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
                         tile_start, slot_start, part_out, part_lse, workers, st_};
         const GqaGeom g = gqa_geom(d, hkv, rows);
-        const hipError_t e = tg ? dispatch_gqa_tg(d, rows, gqa_tg_waves(b * hkv, d), a)
+        const hipError_t e = tg ? dispatch_gqa_tg(d, rows, gqa_tg_waves(workers * hkv, d), a)
                              : d == 64 ? dispatch_gqa_mfma<64>(g, a)
                              : d == 128 ? dispatch_gqa_mfma<128>(g, a)
                                         : dispatch_gqa_mfma<256>(g, a);

@@ -617,17 +617,22 @@ __global__ void __launch_bounds__(64 * HPB * RG, 1)
 }
 
 // ----------------------------------------------------------------------------
-// Token-group kernel (one block per sequence and KV head, no split-KV).
+// Token-group kernel: one head per block, the block's waves split the tokens.
 //
-// When the batch alone has a block for every CU (b * hkv >= CUs) no sequence
-// needs to be split over blocks, and the combine launch and the partials can be
-// dropped. A block is then one (sequence, KV head); its TG waves take the
-// sequence's 16-token stages round robin (wave w: stages w, w + TG, ...), each
+// A block is one (worker, KV head). Its worker's cache range is walked piece by
+// piece, a piece being the worker's tiles of one sequence; the TG waves take
+// the piece's 16-token stages round robin (wave w: stages w, w + TG, ...), each
 // through a ring of its own in LDS, so the loop has no barrier: a wave waits
-// only for its own copies (vmcnt). At the end the waves' softmax states
-// (reference maximum, sum, unnormalised accumulators) meet in LDS and are
-// merged per row. The per-stage arithmetic and the LDS layout are those of the
-// MFMA kernel above with one head per block.
+// only for its own copies (vmcnt). At the end of a piece the waves' softmax
+// states (reference maximum, sum, unnormalised accumulators) meet in LDS and
+// are merged per row into the result, or into the piece's partial for the
+// combine when the sequence is split. The per-stage arithmetic and the LDS
+// layout are those of the MFMA kernel above with one head per block.
+//
+// Without a workspace (hdr == nullptr) worker w is sequence w: one piece per
+// block, no plan arrays, no partials, no combine. That mode is also taken
+// automatically when the batch alone has a block for every CU
+// (b * hkv >= CUs).
 //
 // Ring depth: two stages per wave (one in flight while the other is computed).
 // At the layer's geometry (b = 32, hkv = 8, d = 128, t = 4096; four waves per
@@ -646,9 +651,11 @@ struct GqaTgCfg {
     static constexpr int LWK = LW / 2;              // the first LWK copies are K
     static constexpr int RING = NST * STAGE_BYTES;  // LDS ring of one wave
     static constexpr int RB = RBLK * 16;            // rows per wave (padded)
-    static constexpr int MERGE_BYTES = TG * RB * (D + 2) * 4;
+    static constexpr int ACC_STRIDE = D + 4;        // floats per merged row (padding spreads the banks)
+    static constexpr int MERGE_BYTES = TG * RB * (ACC_STRIDE + 2) * 4;
     static constexpr int LDS_BYTES = TG * RING > MERGE_BYTES ? TG * RING : MERGE_BYTES;
     static constexpr int KS = D / 32, DB = D / 16;
+    static_assert(kGqaTile % T == 0, "planner tiles are whole stages");
     static_assert(NST >= 2 && (NST - 2) * LW <= 63, "outstanding copies fit the vmcnt counter");
     static_assert(LDS_BYTES <= 163840, "LDS of a CU");
 };
@@ -656,16 +663,19 @@ struct GqaTgCfg {
 template <int D, int RBLK, int TG, int NST>
 __global__ void __launch_bounds__(64 * TG, 1)
     gqa_tg_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-                  const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens, int s, int hq, int hkv,
-                  int t_max, float scale_log2, int units, uint16_t *__restrict__ out, float *__restrict__ lse)
+                  const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens, int B, int s, int hq,
+                  int hkv, int t_max, float scale_log2, int units, PlanHeader *__restrict__ hdr,
+                  int *__restrict__ tile_start, int *__restrict__ slot_start, uint16_t *__restrict__ out,
+                  float *__restrict__ lse, uint16_t *__restrict__ part_out, float *__restrict__ part_lse)
 {
     using C = GqaTgCfg<D, RBLK, TG, NST>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     DA_LDS char *lds = (DA_LDS char *)smem;
     const int unit = xcd_linear_unit(blockIdx.x, gridDim.x);
     if (unit >= units) return;
-    const int bq = unit / hkv;
-    const int kvh = unit - bq * hkv;
+    const int worker = unit / hkv;
+    const int kvh = unit - worker * hkv;
+    const int workers = units / hkv;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // token group
     const int lane = tid & 63;
@@ -679,54 +689,27 @@ __global__ void __launch_bounds__(64 * TG, 1)
         const int j = r - i * grp;
         return i * hq + kvh * grp + j;
     };
-    const int L = clamp_len(seqlens[bq], t_max);
-    const int nall = (L + C::T - 1) / C::T;                   // stages of the sequence
-    const int nmine = nall > w ? (nall - w + TG - 1) / TG : 0;  // ... of this wave
+
+    const bool per_seq = hdr == nullptr;
+    if (!per_seq && unit == 0 && tid < 64)
+        write_plan(seqlens, B, t_max, kGqaTile, workers, hdr, tile_start, slot_start);
+    PlanWalk cur;
+    if (per_seq ? !cur.init_per_sequence(seqlens, t_max, kGqaTile, worker)
+                : !cur.init(seqlens, B, t_max, kGqaTile, workers, worker)) {
+        if (per_seq) {
+            // a sequence with no cache row: its rows are out = 0, lse = -inf
+            for (int i = tid; i < R * (D / 8); i += 64 * TG) {
+                const int r = i / (D / 8);
+                *(u32x4 *)(out + ((size_t)worker * M + row_of(r)) * D + (i - r * (D / 8)) * 8) =
+                    u32x4{0u, 0u, 0u, 0u};
+            }
+            for (int r = tid; r < R; r += 64 * TG) lse[(size_t)worker * M + row_of(r)] = -INFINITY;
+        }
+        return;
+    }
+
     DA_LDS char *ring = lds + w * C::RING;
     const int tok_e = hkv * D;  // elements of one token's K (or V) row, all KV heads
-    const u32x4 rsrc_k = raw_buffer_rsrc(kc + (size_t)bq * t_max * tok_e, (uint32_t)(L * tok_e * 2));
-    const u32x4 rsrc_v = raw_buffer_rsrc(vc + (size_t)bq * t_max * tok_e, (uint32_t)(L * tok_e * 2));
-    auto issue = [&](int j) {  // the wave's j-th stage into ring slot j % NST
-        const int tok0 = (w + j * TG) * C::T;
-        DA_LDS char *dst = ring + (j % NST) * C::STAGE_BYTES;
-#pragma unroll
-        for (int i = 0; i < C::LW; ++i) {
-            const bool is_k = i < C::LWK;
-            const int p = (is_k ? i : i - C::LWK) * 64 + lane;  // chunk of the K (or V) rows
-            const int tk = p / C::CPR;
-            const int c = (p - tk * C::CPR) ^ gqa_swz(tk);
-            // rows past L read as zero (out of range: no memory request)
-            const uint32_t off = (uint32_t)(((tok0 + tk) * tok_e + kvh * D) * 2 + c * 16);
-            lds_dma16_stream(is_k ? rsrc_k : rsrc_v, dst + i * 1024, off);
-        }
-    };
-
-    bf16x8 qB[RBLK][C::KS];
-    f32x4 acc[RBLK][C::DB];
-    float mref[RBLK], lsum[RBLK];
-    int nvis[RBLK];
-    int mn = 0x7fffffff;
-#pragma unroll
-    for (int rb = 0; rb < RBLK; ++rb) {
-        const int r = rb * 16 + n;
-        const bool ok = r < R;
-        nvis[rb] = ok ? L - s + r / grp + 1 : 0;  // causal: draft i sees L - s + i + 1 rows
-        mn = min(mn, nvis[rb]);
-#pragma unroll
-        for (int kk = 0; kk < C::KS; ++kk) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (ok) v = *(const u32x4 *)(q + ((size_t)bq * M + row_of(r)) * D + kk * 32 + g * 8);
-            qB[rb][kk] = as_bf16x8(v);
-        }
-        mref[rb] = -INFINITY;
-        lsum[rb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int off = 1; off < 64; off <<= 1) mn = min(mn, __shfl_xor(mn, off));
-    const int nvis_min = mn;
-    wait_vm_loads_visible();
-
     const int qk_base = n * C::ROW;
     const int sq = gqa_swz(n);
     const int tr_tok = 4 * g + (n >> 2);
@@ -734,107 +717,175 @@ __global__ void __launch_bounds__(64 * TG, 1)
     const int hsel = (n & 3) >> 1;
     const int tr_base = C::T * C::ROW + tr_tok * C::ROW + ((n & 1) << 3);
 
-    for (int j = 0; j < min(NST - 1, nmine); ++j) issue(j);
-    for (int j = 0; j < nmine; ++j) {
-        wait_stage_copies<C::LW, NST - 2>(min(NST - 2, nmine - 1 - j));
-        if (j + NST - 1 < nmine) {
-            // the slot refilled now was read in the previous step: those reads are done
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            issue(j + NST - 1);
-        }
-        const int tok0 = (w + j * TG) * C::T;
-        const DA_LDS char *stg = ring + (j % NST) * C::STAGE_BYTES;
-        f32x4 S[RBLK];
+    // One piece: the stages [tok0_piece, tok0_piece + 16 * nall) of sequence bq,
+    // merged at the end into the rows' result (final) or into partial slot sl.
+    auto piece = [&](int bq, int L, int tok0_piece, int nall, bool final_, int sl) {
+        const int nmine = nall > w ? (nall - w + TG - 1) / TG : 0;  // stages of this wave
+        const u32x4 rsrc_k = raw_buffer_rsrc(kc + (size_t)bq * t_max * tok_e, (uint32_t)(L * tok_e * 2));
+        const u32x4 rsrc_v = raw_buffer_rsrc(vc + (size_t)bq * t_max * tok_e, (uint32_t)(L * tok_e * 2));
+        auto issue = [&](int j) {  // the wave's j-th stage into ring slot j % NST
+            const int tok0 = tok0_piece + (w + j * TG) * C::T;
+            DA_LDS char *dst = ring + (j % NST) * C::STAGE_BYTES;
 #pragma unroll
-        for (int rb = 0; rb < RBLK; ++rb) S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < C::KS; ++kk) {
-            const int c = kk * 4 + g;
-            const bf16x8 a = *(const DA_LDS bf16x8 *)(stg + qk_base + ((c ^ sq) << 4));
-#pragma unroll
-            for (int rb = 0; rb < RBLK; ++rb) S[rb] = mfma16x16x32(a, qB[rb][kk], S[rb]);
-        }
-        i16x4 pB[RBLK];
+            for (int i = 0; i < C::LW; ++i) {
+                const bool is_k = i < C::LWK;
+                const int p = (is_k ? i : i - C::LWK) * 64 + lane;  // chunk of the K (or V) rows
+                const int tk = p / C::CPR;
+                const int c = (p - tk * C::CPR) ^ gqa_swz(tk);
+                // rows past L read as zero (out of range: no memory request)
+                const uint32_t off = (uint32_t)(((tok0 + tk) * tok_e + kvh * D) * 2 + c * 16);
+                lds_dma16_stream(is_k ? rsrc_k : rsrc_v, dst + i * 1024, off);
+            }
+        };
+
+        bf16x8 qB[RBLK][C::KS];
+        f32x4 acc[RBLK][C::DB];
+        float mref[RBLK], lsum[RBLK];
+        int nvis[RBLK];
+        int mn = 0x7fffffff;
 #pragma unroll
         for (int rb = 0; rb < RBLK; ++rb) {
-            if (tok0 + C::T > nvis_min) {
+            const int r = rb * 16 + n;
+            const bool ok = r < R;
+            nvis[rb] = ok ? L - s + r / grp + 1 : 0;  // causal: draft i sees L - s + i + 1 rows
+            mn = min(mn, nvis[rb]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (tok0 + g * 4 + i >= nvis[rb]) S[rb][i] = -INFINITY;
+            for (int kk = 0; kk < C::KS; ++kk) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (ok) v = *(const u32x4 *)(q + ((size_t)bq * M + row_of(r)) * D + kk * 32 + g * 8);
+                qB[rb][kk] = as_bf16x8(v);
             }
-            float m = fmaxf(fmaxf(S[rb][0], S[rb][1]), fmaxf(S[rb][2], S[rb][3]));
-            const float mt = wave_max_across_groups16(m) * scale_log2;
-            if (__builtin_amdgcn_ballot_w64(mt > mref[rb] + kRescaleSlack)) {
-                const float mnew = fmaxf(mref[rb], mt);
-                const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref[rb] - mnew);
-                mref[rb] = mnew;
-                lsum[rb] *= alpha;
+            mref[rb] = -INFINITY;
+            lsum[rb] = 0.f;
 #pragma unroll
-                for (int db = 0; db < C::DB; ++db) acc[rb][db] *= alpha;
-            }
-            const float ms = mref[rb] == -INFINITY ? 0.f : mref[rb];
-            float p[4], part = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[i] = fast_exp2(__builtin_fmaf(S[rb][i], scale_log2, -ms));
-                part += p[i];
-            }
-            lsum[rb] += wave_sum_across_groups16(part);
-            const u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-            pB[rb] = __builtin_bit_cast(i16x4, pk);
+            for (int db = 0; db < C::DB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-            const int c = 2 * db + hsel;
-            const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (DA_LDS i16x4 *)(stg + tr_base + ((c ^ st) << 4)));
-#pragma unroll
-            for (int rb = 0; rb < RBLK; ++rb)
-                acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pB[rb], acc[rb][db], 0, 0, 0);
-        }
-    }
+        for (int off = 1; off < 64; off <<= 1) mn = min(mn, __shfl_xor(mn, off));
+        const int nvis_min = mn;
+        wait_vm_loads_visible();
 
-    // ---- merge the token groups: M = max_w m_w, l = sum_w l_w 2^(m_w - M),
-    // O = sum_w O_w 2^(m_w - M) / l, lse = (M + log2 l) ln 2
-    __syncthreads();  // every ring is read: the LDS now holds the states
-    DA_LDS float *macc = (DA_LDS float *)lds;  // [TG][RB][D] unnormalised accumulators
-    DA_LDS float *mm = macc + TG * C::RB * D;  // [TG][RB] reference maxima (log2 domain)
-    DA_LDS float *ml = mm + TG * C::RB;        // [TG][RB] sums
+        for (int j = 0; j < min(NST - 1, nmine); ++j) issue(j);
+        for (int j = 0; j < nmine; ++j) {
+            wait_stage_copies<C::LW, NST - 2>(min(NST - 2, nmine - 1 - j));
+            if (j + NST - 1 < nmine) {
+                // the slot refilled now was read in the previous step: those reads are done
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                issue(j + NST - 1);
+            }
+            const int tok0 = tok0_piece + (w + j * TG) * C::T;
+            const DA_LDS char *stg = ring + (j % NST) * C::STAGE_BYTES;
+            f32x4 S[RBLK];
 #pragma unroll
-    for (int rb = 0; rb < RBLK; ++rb) {
-        const int r = rb * 16 + n;
+            for (int rb = 0; rb < RBLK; ++rb) S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-            *(DA_LDS f32x4 *)(macc + (w * C::RB + r) * D + db * 16 + g * 4) = acc[rb][db];
-        if (g == 0) {
-            mm[w * C::RB + r] = mref[rb];
-            ml[w * C::RB + r] = lsum[rb];
-        }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < R * (D / 4); idx += 64 * TG) {
-        const int r = idx / (D / 4);
-        const int c4 = idx - r * (D / 4);
-        float mx = -INFINITY;
+            for (int kk = 0; kk < C::KS; ++kk) {
+                const int c = kk * 4 + g;
+                const bf16x8 a = *(const DA_LDS bf16x8 *)(stg + qk_base + ((c ^ sq) << 4));
 #pragma unroll
-        for (int t = 0; t < TG; ++t) mx = fmaxf(mx, mm[t * C::RB + r]);
-        float l = 0.f;
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        if (mx != -INFINITY) {
+                for (int rb = 0; rb < RBLK; ++rb) S[rb] = mfma16x16x32(a, qB[rb][kk], S[rb]);
+            }
+            i16x4 pB[RBLK];
 #pragma unroll
-            for (int t = 0; t < TG; ++t) {
-                const float f = fast_exp2(mm[t * C::RB + r] - mx);
-                l += ml[t * C::RB + r] * f;
-                a += *(const DA_LDS f32x4 *)(macc + (t * C::RB + r) * D + c4 * 4) * f;
+            for (int rb = 0; rb < RBLK; ++rb) {
+                if (tok0 + C::T > nvis_min) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (tok0 + g * 4 + i >= nvis[rb]) S[rb][i] = -INFINITY;
+                }
+                float m = fmaxf(fmaxf(S[rb][0], S[rb][1]), fmaxf(S[rb][2], S[rb][3]));
+                const float mt = wave_max_across_groups16(m) * scale_log2;
+                if (__builtin_amdgcn_ballot_w64(mt > mref[rb] + kRescaleSlack)) {
+                    const float mnew = fmaxf(mref[rb], mt);
+                    const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref[rb] - mnew);
+                    mref[rb] = mnew;
+                    lsum[rb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) acc[rb][db] *= alpha;
+                }
+                const float ms = mref[rb] == -INFINITY ? 0.f : mref[rb];
+                float p[4], part = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = fast_exp2(__builtin_fmaf(S[rb][i], scale_log2, -ms));
+                    part += p[i];
+                }
+                lsum[rb] += wave_sum_across_groups16(part);
+                const u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+                pB[rb] = __builtin_bit_cast(i16x4, pk);
+            }
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+                const int c = 2 * db + hsel;
+                const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (DA_LDS i16x4 *)(stg + tr_base + ((c ^ st) << 4)));
+#pragma unroll
+                for (int rb = 0; rb < RBLK; ++rb)
+                    acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pB[rb], acc[rb][db], 0, 0, 0);
             }
         }
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        const int row = row_of(r);
-        u32x2 v;
-        v[0] = pack_bf16x2(a[0] * inv, a[1] * inv);
-        v[1] = pack_bf16x2(a[2] * inv, a[3] * inv);
-        *(u32x2 *)(out + ((size_t)bq * M + row) * D + c4 * 4) = v;
-        if (c4 == 0) lse[(size_t)bq * M + row] = l > 0.f ? (mx + fast_log2(l)) * kLn2 : -INFINITY;
+
+        // ---- merge the token groups: M = max_w m_w, l = sum_w l_w 2^(m_w - M),
+        // O = sum_w O_w 2^(m_w - M) / l, lse2 = M + log2 l
+        __syncthreads();  // every ring is read: the LDS now holds the states
+        DA_LDS float *macc = (DA_LDS float *)lds;            // [TG][RB][ACC_STRIDE] unnormalised accumulators
+        DA_LDS float *mm = macc + TG * C::RB * C::ACC_STRIDE;  // [TG][RB] reference maxima (log2 domain)
+        DA_LDS float *ml = mm + TG * C::RB;                  // [TG][RB] sums
+#pragma unroll
+        for (int rb = 0; rb < RBLK; ++rb) {
+            const int r = rb * 16 + n;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+                *(DA_LDS f32x4 *)(macc + (w * C::RB + r) * C::ACC_STRIDE + db * 16 + g * 4) = acc[rb][db];
+            if (g == 0) {
+                mm[w * C::RB + r] = mref[rb];
+                ml[w * C::RB + r] = lsum[rb];
+            }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < R * (D / 4); idx += 64 * TG) {
+            const int r = idx / (D / 4);
+            const int c4 = idx - r * (D / 4);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < TG; ++t) mx = fmaxf(mx, mm[t * C::RB + r]);
+            float l = 0.f;
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            if (mx != -INFINITY) {
+#pragma unroll
+                for (int t = 0; t < TG; ++t) {
+                    const float f = fast_exp2(mm[t * C::RB + r] - mx);
+                    l += ml[t * C::RB + r] * f;
+                    a += *(const DA_LDS f32x4 *)(macc + (t * C::RB + r) * C::ACC_STRIDE + c4 * 4) * f;
+                }
+            }
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const float lse2 = l > 0.f ? mx + fast_log2(l) : -INFINITY;
+            const int row = row_of(r);
+            u32x2 v;
+            v[0] = pack_bf16x2(a[0] * inv, a[1] * inv);
+            v[1] = pack_bf16x2(a[2] * inv, a[3] * inv);
+            // the result, or this piece's bf16 partial (normalised by its own sum) for the combine
+            if (final_) {
+                *(u32x2 *)(out + ((size_t)bq * M + row) * D + c4 * 4) = v;
+                if (c4 == 0) lse[(size_t)bq * M + row] = lse2 * kLn2;
+            } else {
+                *(u32x2 *)(part_out + ((size_t)sl * M + row) * D + c4 * 4) = v;
+                if (c4 == 0) part_lse[(size_t)sl * M + row] = lse2;
+            }
+        }
+        __syncthreads();  // the merge's LDS reads are done before the next piece's copies land
+    };
+
+    // the worker's pieces: its tiles of each sequence it touches
+    for (int tt = cur.tile_lo; tt < cur.tile_hi;) {
+        cur.seek(seqlens, tt);
+        const int bq = cur.b;
+        const int t_end = min(cur.tile_hi, cur.te);
+        const int L = clamp_len(seqlens[bq], t_max);
+        const int tok_lo = (tt - cur.ts) * kGqaTile;
+        const int tok_hi = min(L, (t_end - cur.ts) * kGqaTile);
+        piece(bq, L, tok_lo, (tok_hi - tok_lo + C::T - 1) / C::T, cur.ns == 1, cur.ns == 1 ? 0 : cur.slot(worker));
+        tt = t_end;
     }
 }
 
