@@ -740,6 +740,8 @@ __global__ void __launch_bounds__(64 * TG, 1)
 
         bf16x8 qB[RBLK][C::KS];
         f32x4 acc[RBLK][C::DB];
+        // mref: the row's reference maximum (log2 units), identical on its four lanes; lsum: this
+        // lane's share of the row's sum (its tokens only), reduced across the lanes once per piece
         float mref[RBLK], lsum[RBLK];
         int nvis[RBLK];
         int mn = 0x7fffffff;
@@ -784,7 +786,11 @@ __global__ void __launch_bounds__(64 * TG, 1)
 #pragma unroll
                 for (int rb = 0; rb < RBLK; ++rb) S[rb] = mfma16x16x32(a, qB[rb][kk], S[rb]);
             }
-            i16x4 pB[RBLK];
+            // mask, then a lane-local test whether any reference must move (rare: mostly
+            // the first stages of a piece); only then is the row maximum formed across
+            // the row's four lanes
+            float mloc[RBLK];
+            bool need = false;
 #pragma unroll
             for (int rb = 0; rb < RBLK; ++rb) {
                 if (tok0 + C::T > nvis_min) {
@@ -792,24 +798,31 @@ __global__ void __launch_bounds__(64 * TG, 1)
                     for (int i = 0; i < 4; ++i)
                         if (tok0 + g * 4 + i >= nvis[rb]) S[rb][i] = -INFINITY;
                 }
-                float m = fmaxf(fmaxf(S[rb][0], S[rb][1]), fmaxf(S[rb][2], S[rb][3]));
-                const float mt = wave_max_across_groups16(m) * scale_log2;
-                if (__builtin_amdgcn_ballot_w64(mt > mref[rb] + kRescaleSlack)) {
-                    const float mnew = fmaxf(mref[rb], mt);
-                    const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref[rb] - mnew);
-                    mref[rb] = mnew;
-                    lsum[rb] *= alpha;
+                mloc[rb] = fmaxf(fmaxf(S[rb][0], S[rb][1]), fmaxf(S[rb][2], S[rb][3])) * scale_log2;
+                need |= mloc[rb] > mref[rb] + kRescaleSlack;
+            }
+            if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-                    for (int db = 0; db < C::DB; ++db) acc[rb][db] *= alpha;
+                for (int rb = 0; rb < RBLK; ++rb) {
+                    const float mt = wave_max_across_groups16(mloc[rb]);
+                    if (__builtin_amdgcn_ballot_w64(mt > mref[rb] + kRescaleSlack)) {
+                        const float mnew = fmaxf(mref[rb], mt);
+                        const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref[rb] - mnew);
+                        mref[rb] = mnew;
+                        lsum[rb] *= alpha;
+#pragma unroll
+                        for (int db = 0; db < C::DB; ++db) acc[rb][db] *= alpha;
+                    }
                 }
+            }
+            i16x4 pB[RBLK];
+#pragma unroll
+            for (int rb = 0; rb < RBLK; ++rb) {
                 const float ms = mref[rb] == -INFINITY ? 0.f : mref[rb];
-                float p[4], part = 0.f;
+                float p[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[i] = fast_exp2(__builtin_fmaf(S[rb][i], scale_log2, -ms));
-                    part += p[i];
-                }
-                lsum[rb] += wave_sum_across_groups16(part);
+                for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(S[rb][i], scale_log2, -ms));
+                lsum[rb] += (p[0] + p[1]) + (p[2] + p[3]);
                 const u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
                 pB[rb] = __builtin_bit_cast(i16x4, pk);
             }
@@ -833,12 +846,13 @@ __global__ void __launch_bounds__(64 * TG, 1)
 #pragma unroll
         for (int rb = 0; rb < RBLK; ++rb) {
             const int r = rb * 16 + n;
+            const float ltot = wave_sum_across_groups16(lsum[rb]);  // the row's sum over its four lanes
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
                 *(DA_LDS f32x4 *)(macc + (w * C::RB + r) * C::ACC_STRIDE + db * 16 + g * 4) = acc[rb][db];
             if (g == 0) {
                 mm[w * C::RB + r] = mref[rb];
-                ml[w * C::RB + r] = lsum[rb];
+                ml[w * C::RB + r] = ltot;
             }
         }
         __syncthreads();
