@@ -14,12 +14,12 @@ finds its inputs cached by the previous call of the same part.
 Prints ONE JSON line: value = algorithmic TFLOP/s of the step (closed-form
 FLOPs / wall time per step over the K timed steps, which have no marker
 between calls), plus
-  parts      per-call times inside the step: the unmarked K steps minus the
-             unmarked K steps without that call; and from HIP events at
-             every call boundary over another pass (each marker adds a
-             dispatch gap);
+  parts      per-call times from HIP events at every call boundary over a
+             pass of the K steps (marked_us; each marker adds a dispatch
+             gap) and less the mean gap (us);
   timing     per part, the median per-launch time of 5 batches of 20 launches,
              with and without input rotation;
+  ceilings   the HBM read rate this GPU attains (a streaming-read probe);
   roofline   the dominant call placed on the MI355X roofline, with `traffic`
              = HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
              of this same invocation (child processes, before this process
@@ -176,30 +176,6 @@ def time_steps(parts, steps, warmup):
     return wall, a.elapsed_time(b) / 1e3 / steps
 
 
-def time_marginal(parts, steps, reps=3):
-    """Each call's time inside the step without any marker between calls: the K steps timed with HIP events
-    at their two ends only, once with every part and once with each part left out (median of `reps`
-    repetitions of each); a call's time is the difference. Returns {name: seconds}."""
-    stream = torch.cuda.current_stream()
-
-    def run(ps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for p in ps:
-            p(0)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for k in range(steps):
-            for p in ps:
-                p(k)
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) / 1e3 / steps
-
-    full = statistics.median(run(parts) for _ in range(reps))
-    return {p.name: full - statistics.median(run([q for q in parts if q is not p]) for _ in range(reps))
-            for p in parts}
-
-
 def time_calls(parts, steps):
     """Per-call breakdown of the step with markers: the same K steps once more with one HIP event on the
     library's stream at every boundary between consecutive calls, so a call's time is the difference of
@@ -242,6 +218,42 @@ def time_batches(part, rotate=True, batches=BATCHES, launches=LAUNCHES, warmup=3
         b.synchronize()
         res.append(a.elapsed_time(b) / 1e3 / launches)
     return statistics.median(res), res
+
+
+def read_ceiling(dev, reps=10):
+    """HBM bytes per second of one streaming read of 1 GiB: the read-rate probe library built beside the
+    decode library (non-temporal 16-byte loads, grid-stride), best of three launch shapes; two buffers
+    alternate so that no launch finds its bytes in the last-level cache."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(binding.library_path()), "libda_read_probe.so"))
+    lib.da_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
+    lib.da_probe_read.restype = ctypes.c_int
+    nbytes = 1 << 30
+    bufs = [torch.full((nbytes,), i + 1, dtype=torch.uint8, device=dev) for i in range(2)]
+    shapes = ((256, 8), (512, 4), (1024, 2))  # blocks of 256 threads, loads in flight per thread
+    sink = torch.empty(max(b for b, _ in shapes) * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = 0.0
+    for blocks, unroll in shapes:
+        def run(i):
+            rc = lib.da_probe_read(ctypes.c_void_p(bufs[i % 2].data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                   blocks, unroll, ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError("read probe launch failed: HIP error %d" % rc)
+        for i in range(3):
+            run(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            run(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, nbytes * reps / (e0.elapsed_time(e1) / 1e3))
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return best
 
 
 def measured_ceilings(dev, reps=20):
@@ -407,6 +419,7 @@ def sweep_key(dev):
         del p
         torch.cuda.empty_cache()
     bw, fl = measured_ceilings(dev)
+    rd = read_ceiling(dev)
     sh = wl.mla_mtp(1)
     best = max(tf for _, tf in us.values()) * 1e12
     cross = lambda f, b: round(cm.mla_ridge_crossing_s(sh.h, sh.k, sh.p, sh.t_max, peak_flops=f, bw=b), 3)  # noqa
@@ -414,6 +427,8 @@ def sweep_key(dev):
                "spec_crossing_s": cross(cm.MI355X_BF16_FLOPS, cm.MI355X_HBM_BYTES_PER_S),
                "measured_copy_tbs": round(bw / 1e12, 3), "measured_gemm_tflops": round(fl / 1e12, 1),
                "measured_ridge_flop_per_byte": round(fl / bw, 1), "measured_crossing_s": cross(fl, bw),
+               "measured_read_tbs": round(rd / 1e12, 3), "read_ridge_flop_per_byte": round(fl / rd, 1),
+               "read_crossing_s": cross(fl, rd),
                "kernel_best_tflops": round(best / 1e12, 1), "kernel_crossing_s": cross(best, bw),
                "time_vs_s1": {str(s): round(t / us[1][0], 3) for s, (t, _) in sorted(us.items())}}
     return {"workload": "mla_mtp (b=32, h=128, k=512, p=64, t=4096, s drafts; rotating inputs, median of %d x %d)"
@@ -675,22 +690,28 @@ def main():
         timing[p.name] = {"rotating_median_us": round(rot * 1e6, 2), "same_input_median_us": round(same * 1e6, 2),
                           "rotating_batches_us": [round(x * 1e6, 2) for x in rot_all],
                           "same_input_batches_us": [round(x * 1e6, 2) for x in same_all]}
-    # per-call breakdowns first (marked pass, then the unmarked differences), then the W warmup and the K
-    # timed steps, which are thus the last calls of the run
+    # the per-call breakdown first (the marked pass), then the W warmup and the K timed steps, which are
+    # thus the last calls of the run
     marked = time_calls(parts, args.steps)
-    per = time_marginal(parts, args.steps) if len(parts) > 1 else marked
     wall, ev_step = time_steps(parts, args.steps, args.warmup)
+    # a call's time inside the step: its marked time less the mean gap one marker adds, i.e. the marked
+    # pass's excess over the unmarked step spread evenly over the calls (the kernel trace shows equal gaps)
+    gap = max(0.0, (sum(marked.values()) - ev_step) / len(parts))
+    per = {n: v - gap for n, v in marked.items()}
+    read_bw = read_ceiling(dev)
 
     flops = sum(p.cost.flops for p in parts)
     byts = sum(p.cost.bytes for p in parts)
     dom = max(parts, key=lambda p: per[p.name])
     roof = dom.roofline(per[dom.name])
     roof["traffic"] = traffic[dom.name]["bytes_per_call"] if traffic and dom.name in traffic else None
-    roof["kernel"] = dom.name + (" (one call inside the step: K unmarked steps minus K unmarked steps without "
-                                 "it, HIP events; the call is the tile kernel alone at this shape)")
+    roof["kernel"] = dom.name + (" (one call inside the step from HIP events at the call boundaries over K steps, "
+                                 "less the mean marker gap; the call is the tile kernel alone at this shape)")
     part_info = {}
     for p in parts:
         part_info[p.name] = dict(p.summary(per[p.name]), copies=p.copies, marked_us=round(marked[p.name] * 1e6, 2))
+        if p.bound == "hbm":
+            part_info[p.name]["of_measured_read"] = round(p.cost.bytes / per[p.name] / read_bw, 4)
         if traffic and p.name in traffic:
             part_info[p.name]["traffic"] = traffic[p.name]["bytes_per_call"]
             part_info[p.name]["traffic_over_algorithmic"] = round(traffic[p.name]["bytes_per_call"] / p.cost.bytes, 3)
@@ -715,10 +736,13 @@ def main():
         "hbm_tbs": round(byts / wall / 1e12, 3),
         "step_roofline_frac": round(sum(p.t_min for p in parts) / wall, 4),
         "roofline": roof,
+        "ceilings": {"measured_read_tbs": round(read_bw / 1e12, 3), "spec_hbm_tbs": PEAK_GBS / 1e3,
+                     "note": "measured_read: one streaming read of 1 GiB by the read-rate probe, best of three "
+                             "launch shapes; of_measured_read in a part = its algorithmic bytes per second over it"},
         "parts": part_info,
-        "parts_note": ("us: a call's time inside the step with no marker between calls (K unmarked steps minus K "
-                       "unmarked steps without that call, medians of 3); marked_us: HIP events at every call "
-                       "boundary over another pass of the K steps, each marker adding a dispatch gap"),
+        "parts_note": ("marked_us: HIP events at every call boundary over a pass of K steps, each marker adding a "
+                       "dispatch gap; us: marked_us less the mean gap (the marked pass's excess over the unmarked "
+                       "timed step, %.2f us, spread evenly over the calls)" % (gap * 1e6)),
         "timing": dict(timing, protocol="per-launch time, median of %d batches of %d launches; rotating = each "
                                         "launch takes the next of the part's input copies (together > 512 MB)"
                                         % (BATCHES, LAUNCHES)),

@@ -1,4 +1,5 @@
-"""Build the gfx950 shared library libdecode_attn.so in-tree with hipcc.
+"""Build the gfx950 shared library libdecode_attn.so in-tree with hipcc, and the
+benchmark's HBM read-rate probe libda_read_probe.so beside it.
 
     python -m decode_attention_bf16_amd.build          # build
     python -m decode_attention_bf16_amd.build --asm    # also keep the AMDGPU assembly in _build/
@@ -18,6 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "decode_attn.hip")
 LIB = os.path.join(HERE, "libdecode_attn.so")
+PROBE_SRC = os.path.join(HERE, "csrc", "read_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libda_read_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -43,6 +46,9 @@ def build(asm: bool = False, verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, cwd=cwd)
     os.replace(tmp, LIB)
+    ptmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    subprocess.run([HIPCC] + FLAGS + [PROBE_SRC, "-o", ptmp], check=True, cwd=HERE)
+    os.replace(ptmp, PROBE_LIB)
     return LIB
 
 
