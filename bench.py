@@ -225,7 +225,7 @@ def read_ceiling(dev, reps=10):
     decode library (non-temporal 16-byte loads, grid-stride), best of three launch shapes; two buffers
     alternate so that no launch finds its bytes in the last-level cache."""
     import ctypes
-    lib = ctypes.CDLL(os.path.join(os.path.dirname(binding.library_path()), "libda_read_probe.so"))
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(binding.__file__)), "libda_read_probe.so"))
     lib.da_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_void_p]
     lib.da_probe_read.restype = ctypes.c_int
