@@ -738,6 +738,10 @@ __global__ void __launch_bounds__(64 * TG, 1)
             }
         };
 
+        // the first stages' copies go out before the query loads, so that both are in
+        // flight together and the wait for the queries below finds the stages landed too
+        for (int j = 0; j < min(NST - 1, nmine); ++j) issue(j);
+
         bf16x8 qB[RBLK][C::KS];
         f32x4 acc[RBLK][C::DB];
         // mref: the row's reference maximum (log2 units), identical on its four lanes; lsum: this
@@ -766,7 +770,6 @@ __global__ void __launch_bounds__(64 * TG, 1)
         const int nvis_min = mn;
         wait_vm_loads_visible();
 
-        for (int j = 0; j < min(NST - 1, nmine); ++j) issue(j);
         for (int j = 0; j < nmine; ++j) {
             wait_stage_copies<C::LW, NST - 2>(min(NST - 2, nmine - 1 - j));
             if (j + NST - 1 < nmine) {
