@@ -690,7 +690,25 @@ __global__ void __launch_bounds__(64 * TG, 1)
         return i * hq + kvh * grp + j;
     };
 
+    // the queries of this head's rows in sequence bq, as the B operands of the score MFMAs.
+    // Padding rows (r >= R) load the last real row: their scores are masked (no visible
+    // row) and never written, and loads without a branch leave the compiler no join at
+    // which it would wait for them.
+    bf16x8 qB[RBLK][C::KS];
+    auto load_q = [&](int bq) {
+#pragma unroll
+        for (int rb = 0; rb < RBLK; ++rb) {
+            const int r = min(rb * 16 + n, R - 1);
+#pragma unroll
+            for (int kk = 0; kk < C::KS; ++kk)
+                qB[rb][kk] = as_bf16x8(*(const u32x4 *)(q + ((size_t)bq * M + row_of(r)) * D + kk * 32 + g * 8));
+        }
+    };
+
     const bool per_seq = hdr == nullptr;
+    // per sequence, the queries do not depend on the sequence's length: their loads are in
+    // flight while the length is read
+    if (per_seq) load_q(worker);
     if (!per_seq && unit == 0 && tid < 64)
         write_plan(seqlens, B, t_max, kGqaTile, workers, hdr, tile_start, slot_start);
     PlanWalk cur;
@@ -741,8 +759,8 @@ __global__ void __launch_bounds__(64 * TG, 1)
         // the first stages' copies go out before the query loads, so that both are in
         // flight together and the wait for the queries below finds the stages landed too
         for (int j = 0; j < min(NST - 1, nmine); ++j) issue(j);
+        if (!per_seq) load_q(bq);
 
-        bf16x8 qB[RBLK][C::KS];
         f32x4 acc[RBLK][C::DB];
         // mref: the row's reference maximum (log2 units), identical on its four lanes; lsum: this
         // lane's share of the row's sum (its tokens only), reduced across the lanes once per piece
@@ -755,12 +773,6 @@ __global__ void __launch_bounds__(64 * TG, 1)
             const bool ok = r < R;
             nvis[rb] = ok ? L - s + r / grp + 1 : 0;  // causal: draft i sees L - s + i + 1 rows
             mn = min(mn, nvis[rb]);
-#pragma unroll
-            for (int kk = 0; kk < C::KS; ++kk) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (ok) v = *(const u32x4 *)(q + ((size_t)bq * M + row_of(r)) * D + kk * 32 + g * 8);
-                qB[rb][kk] = as_bf16x8(v);
-            }
             mref[rb] = -INFINITY;
             lsum[rb] = 0.f;
 #pragma unroll
