@@ -19,7 +19,8 @@ between calls), plus
              gap) and less the mean gap (us);
   timing     per part, the median per-launch time of 5 batches of 20 launches,
              with and without input rotation;
-  ceilings   the HBM read rate this GPU attains (a streaming-read probe);
+  ceilings   the HBM read rate (a streaming-read probe) and the bf16 GEMM rate
+             (vendor library) this GPU attains;
   roofline   the dominant call placed on the MI355X roofline, with `traffic`
              = HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
              of this same invocation (child processes, before this process
@@ -256,31 +257,45 @@ def read_ceiling(dev, reps=10):
     return best
 
 
+def gemm_ceiling(dev, reps=20, n=12288):
+    """bf16 FLOP/s of an n^3 GEMM through the vendor library: the matrix rate this GPU sustains for a plain
+    product (a reference point, not the decode path)."""
+    x = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    y = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(x, y)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    rate = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) / 1e3)
+    del x, y
+    torch.cuda.empty_cache()
+    return rate
+
+
 def measured_ceilings(dev, reps=20):
     """What this GPU attains, as reference points for the ridge (not the decode path): HBM bytes per
     second of a 1 GiB device-to-device copy (read + write), and bf16 FLOP/s of a 12288^3 GEMM through
     the vendor library."""
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
-    n = 12288
-    x = torch.randn(n, n, device=dev).to(torch.bfloat16)
-    y = torch.randn(n, n, device=dev).to(torch.bfloat16)
-    res = {}
-    for name, fn, work in (("copy", lambda: b.copy_(a), 2.0 * a.numel()),
-                           ("gemm", lambda: torch.matmul(x, y), 2.0 * n ** 3)):
-        for _ in range(3):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        res[name] = work * reps / (e0.elapsed_time(e1) / 1e3)
-    del a, b, x, y
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 2.0 * a.numel() * reps / (e0.elapsed_time(e1) / 1e3)
+    del a, b
     torch.cuda.empty_cache()
-    return res["copy"], res["gemm"]
+    return copy, gemm_ceiling(dev, reps)
 
 
 # ------------------------------------------------------------------ parity and the CPU baseline
@@ -699,11 +714,15 @@ def main():
     gap = max(0.0, (sum(marked.values()) - ev_step) / len(parts))
     per = {n: v - gap for n, v in marked.items()}
     read_bw = read_ceiling(dev)
+    gemm_fl = gemm_ceiling(dev)
 
     flops = sum(p.cost.flops for p in parts)
     byts = sum(p.cost.bytes for p in parts)
     dom = max(parts, key=lambda p: per[p.name])
     roof = dom.roofline(per[dom.name])
+    measured = gemm_fl / 1e12 if roof["bound"] == "mfma" else read_bw / 1e9
+    roof["measured_peak"] = round(measured, 1)
+    roof["frac_of_measured"] = round(roof["achieved"] / measured, 4)
     roof["traffic"] = traffic[dom.name]["bytes_per_call"] if traffic and dom.name in traffic else None
     roof["kernel"] = dom.name + (" (one call inside the step from HIP events at the call boundaries over K steps, "
                                  "less the mean marker gap; the call is the tile kernel alone at this shape)")
@@ -712,6 +731,8 @@ def main():
         part_info[p.name] = dict(p.summary(per[p.name]), copies=p.copies, marked_us=round(marked[p.name] * 1e6, 2))
         if p.bound == "hbm":
             part_info[p.name]["of_measured_read"] = round(p.cost.bytes / per[p.name] / read_bw, 4)
+        else:
+            part_info[p.name]["of_measured_gemm"] = round(p.cost.flops / per[p.name] / gemm_fl, 4)
         if traffic and p.name in traffic:
             part_info[p.name]["traffic"] = traffic[p.name]["bytes_per_call"]
             part_info[p.name]["traffic_over_algorithmic"] = round(traffic[p.name]["bytes_per_call"] / p.cost.bytes, 3)
@@ -737,8 +758,10 @@ def main():
         "step_roofline_frac": round(sum(p.t_min for p in parts) / wall, 4),
         "roofline": roof,
         "ceilings": {"measured_read_tbs": round(read_bw / 1e12, 3), "spec_hbm_tbs": PEAK_GBS / 1e3,
+                     "measured_gemm_tflops": round(gemm_fl / 1e12, 1), "spec_bf16_tflops": PEAK_TFLOPS,
                      "note": "measured_read: one streaming read of 1 GiB by the read-rate probe, best of three "
-                             "launch shapes; of_measured_read in a part = its algorithmic bytes per second over it"},
+                             "launch shapes; measured_gemm: a 12288^3 bf16 GEMM through the vendor library; a "
+                             "part's of_measured_read / of_measured_gemm = its algorithmic rate over them"},
         "parts": part_info,
         "parts_note": ("marked_us: HIP events at every call boundary over a pass of K steps, each marker adding a "
                        "dispatch gap; us: marked_us less the mean gap (the marked pass's excess over the unmarked "
