@@ -177,8 +177,10 @@ int gqa_head_blocks(int hkv) { return (hkv + 3) / 4; }
 int gqa_choose_path(int rows, int path);
 bool gqa_tg_ok(int d, int rows);
 
-// Launch shape of the MFMA kernel: KV heads per block, row-group waves per
-// head and 16-row blocks per wave. The default block holds kBase heads with
+// Launch shape of the head-block MFMA kernel (the shapes the token-group
+// kernel does not take: d = 64, and more rows per KV head than one of its
+// waves holds): KV heads per block, row-group waves per head and 16-row blocks
+// per wave. The default block holds kBase heads with
 // one wave each (all rows of a head in that wave); when hkv is not a multiple
 // of kBase, or a head has more rows than one wave holds, a block takes the
 // fewest heads a whole LDS token row allows (kMin) and spreads each head's
@@ -255,8 +257,8 @@ int gqa_workers(int b, int hkv, int d, int rows, int path, int t_max, int reques
         const GqaGeom g = gqa_geom(d, hkv, rows);
         // resident blocks per CU: the LDS ring allows several; one per CU
         // measured fastest for both shapes (default heads per block, and one
-        // head per block with its rows over several waves: MQA at hq = 64,
-        // 512 workers 39.9 us, 256 workers 36.9 us)
+        // head per block with its rows over several waves: MQA at hq = 64 on
+        // this kernel, 512 workers 39.9 us, 256 workers 36.9 us)
         int per_cu = std::min(163840 / gqa_mfma_lds(d, g), 1);
         if (per_cu < 1) per_cu = 1;
         w = per_cu * current_cu_count() / ((hkv + g.hpb - 1) / g.hpb);
