@@ -449,9 +449,10 @@ def gqa_full_cases(oracle_mod):
 
 @pytest.mark.parametrize("name,path,workers", [("gqa_layer", 1, 0), ("gqa_layer", 2, 0), ("gqa_layer", 2, 128),
                                                ("gqa_mqa", 0, 0), ("gqa_mha", 1, 0), ("gqa_mha", 2, 0),
-                                               ("gqa_mha", 2, 64)])
+                                               ("gqa_mha", 2, 64), ("gqa_mtp4", 0, 0), ("gqa_mtp4", 0, 96)])
 def test_gqa_full_size(da, gqa_full_cases, name, path, workers):
-    """Every row of the full-size grouped workloads: the layer (group 8), MQA and MHA at b=32/8, t=4096.
+    """Every row of the full-size grouped workloads: the layer (group 8, also with 4 drafts), MQA and MHA at
+    b=32/8, t=4096.
     The automatic worker count runs the layer and MHA one block per (sequence, KV head); an explicit
     worker count runs the split-KV kernel and the combine."""
     shape, tensors, ref_o, ref_l = gqa_full_cases(name)

@@ -71,6 +71,9 @@ MTP_SWEEP = (1, 2, 4, 8, 16, 32)
 # shared by all 64 query heads, and 64 KV heads, one per query head (b=8 keeps its cache at 1 GiB).
 GQA_MQA = GQAShape(b=32, s=1, hq=64, hkv=1, d=128, t_max=4096, scale=1.0 / math.sqrt(128), seed=8)
 GQA_MHA = GQAShape(b=8, s=1, hq=64, hkv=64, d=128, t_max=4096, scale=1.0 / math.sqrt(128), seed=9)
+# The layer's geometry with 4 draft tokens per sequence (the MTP step of "Why MLA and MTP Fight Each Other"
+# applied to the grouped layer): 32 query rows per KV head under the drafts' causal mask.
+GQA_MTP4 = GQAShape(b=32, s=4, hq=64, hkv=8, d=128, t_max=4096, scale=1.0 / math.sqrt(128), seed=10)
 # The grouped geometry of the "MQA, GQA & MLA" lesson ("01 · Concept": 24 query heads in 4 groups of 6,
 # head dimension 256) at that page's full context: its 16 GiB per sequence over 16 caching layers at
 # 4 KiB per token per layer is 262,144 tokens. One sequence, one layer: K and V are 512 MiB each.
@@ -90,6 +93,7 @@ WORKLOADS = {
     "mla_ragged": MLA_RAGGED,
     "gqa_mqa": GQA_MQA,
     "gqa_mha": GQA_MHA,
+    "gqa_mtp4": GQA_MTP4,
 }
 
 
