@@ -19,8 +19,9 @@ between calls), plus
              gap) and less the mean gap (us);
   timing     per part, the median per-launch time of 5 batches of 20 launches,
              with and without input rotation;
-  ceilings   the HBM read rate (a streaming-read probe) and the bf16 GEMM rate
-             (vendor library) this GPU attains;
+  ceilings   the HBM read rate and the bf16 MFMA rate this GPU attains (probe
+             kernels: a streaming read, a register-only MFMA loop), and the
+             rate of a vendor-library GEMM;
   roofline   the dominant call placed on the MI355X roofline, with `traffic`
              = HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
              of this same invocation (child processes, before this process
@@ -226,10 +227,7 @@ def read_ceiling(dev, reps=10):
     decode library (non-temporal 16-byte loads, grid-stride), best of three launch shapes; two buffers
     alternate so that no launch finds its bytes in the last-level cache."""
     import ctypes
-    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(binding.__file__)), "libda_read_probe.so"))
-    lib.da_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                  ctypes.c_void_p]
-    lib.da_probe_read.restype = ctypes.c_int
+    lib = _probe_lib()
     nbytes = 1 << 30
     bufs = [torch.full((nbytes,), i + 1, dtype=torch.uint8, device=dev) for i in range(2)]
     shapes = ((256, 8), (512, 4), (1024, 2))  # blocks of 256 threads, loads in flight per thread
@@ -255,6 +253,45 @@ def read_ceiling(dev, reps=10):
     del bufs, sink
     torch.cuda.empty_cache()
     return best
+
+
+def _probe_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(binding.__file__)), "libda_read_probe.so"))
+    lib.da_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
+    lib.da_probe_read.restype = ctypes.c_int
+    lib.da_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.da_probe_mfma.restype = ctypes.c_int
+    return lib
+
+
+def mfma_ceiling(dev, reps=5, iters=4000):
+    """bf16 FLOP/s of the probe library's MFMA loop: four waves per SIMD, each running four independent
+    chains of 32x32x16 MFMAs on register operands (no memory traffic), i.e. the matrix rate at the clock
+    the chip sustains under a full matrix load."""
+    import ctypes
+    lib = _probe_lib()
+    blocks = 4 * torch.cuda.get_device_properties(dev).multi_processor_count  # 4 waves per block
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        rc = lib.da_probe_mfma(blocks, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("MFMA probe launch failed: HIP error %d" % rc)
+    for _ in range(2):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    flops = float(blocks) * 4 * iters * 4 * 32768 * reps
+    del sink
+    return flops / (e0.elapsed_time(e1) / 1e3)
 
 
 def gemm_ceiling(dev, reps=20, n=12288):
@@ -435,6 +472,7 @@ def sweep_key(dev):
         torch.cuda.empty_cache()
     bw, fl = measured_ceilings(dev)
     rd = read_ceiling(dev)
+    mf = mfma_ceiling(dev)
     sh = wl.mla_mtp(1)
     best = max(tf for _, tf in us.values()) * 1e12
     cross = lambda f, b: round(cm.mla_ridge_crossing_s(sh.h, sh.k, sh.p, sh.t_max, peak_flops=f, bw=b), 3)  # noqa
@@ -444,6 +482,8 @@ def sweep_key(dev):
                "measured_ridge_flop_per_byte": round(fl / bw, 1), "measured_crossing_s": cross(fl, bw),
                "measured_read_tbs": round(rd / 1e12, 3), "read_ridge_flop_per_byte": round(fl / rd, 1),
                "read_crossing_s": cross(fl, rd),
+               "measured_mfma_tflops": round(mf / 1e12, 1), "mfma_read_ridge_flop_per_byte": round(mf / rd, 1),
+               "mfma_read_crossing_s": cross(mf, rd),
                "kernel_best_tflops": round(best / 1e12, 1), "kernel_crossing_s": cross(best, bw),
                "time_vs_s1": {str(s): round(t / us[1][0], 3) for s, (t, _) in sorted(us.items())}}
     return {"workload": "mla_mtp (b=32, h=128, k=512, p=64, t=4096, s drafts; rotating inputs, median of %d x %d)"
@@ -714,13 +754,14 @@ def main():
     gap = max(0.0, (sum(marked.values()) - ev_step) / len(parts))
     per = {n: v - gap for n, v in marked.items()}
     read_bw = read_ceiling(dev)
+    mfma_fl = mfma_ceiling(dev)
     gemm_fl = gemm_ceiling(dev)
 
     flops = sum(p.cost.flops for p in parts)
     byts = sum(p.cost.bytes for p in parts)
     dom = max(parts, key=lambda p: per[p.name])
     roof = dom.roofline(per[dom.name])
-    measured = gemm_fl / 1e12 if roof["bound"] == "mfma" else read_bw / 1e9
+    measured = mfma_fl / 1e12 if roof["bound"] == "mfma" else read_bw / 1e9
     roof["measured_peak"] = round(measured, 1)
     roof["frac_of_measured"] = round(roof["achieved"] / measured, 4)
     roof["traffic"] = traffic[dom.name]["bytes_per_call"] if traffic and dom.name in traffic else None
@@ -732,6 +773,7 @@ def main():
         if p.bound == "hbm":
             part_info[p.name]["of_measured_read"] = round(p.cost.bytes / per[p.name] / read_bw, 4)
         else:
+            part_info[p.name]["of_measured_mfma"] = round(p.cost.flops / per[p.name] / mfma_fl, 4)
             part_info[p.name]["of_measured_gemm"] = round(p.cost.flops / per[p.name] / gemm_fl, 4)
         if traffic and p.name in traffic:
             part_info[p.name]["traffic"] = traffic[p.name]["bytes_per_call"]
@@ -758,10 +800,13 @@ def main():
         "step_roofline_frac": round(sum(p.t_min for p in parts) / wall, 4),
         "roofline": roof,
         "ceilings": {"measured_read_tbs": round(read_bw / 1e12, 3), "spec_hbm_tbs": PEAK_GBS / 1e3,
+                     "measured_mfma_tflops": round(mfma_fl / 1e12, 1),
                      "measured_gemm_tflops": round(gemm_fl / 1e12, 1), "spec_bf16_tflops": PEAK_TFLOPS,
-                     "note": "measured_read: one streaming read of 1 GiB by the read-rate probe, best of three "
-                             "launch shapes; measured_gemm: a 12288^3 bf16 GEMM through the vendor library; a "
-                             "part's of_measured_read / of_measured_gemm = its algorithmic rate over them"},
+                     "note": "measured_read: one streaming read of 1 GiB by the read probe, best of three launch "
+                             "shapes; measured_mfma: the probe's register-only loop of 32x32x16 bf16 MFMAs on every "
+                             "SIMD; measured_gemm: a 12288^3 bf16 GEMM through the vendor library; a part's "
+                             "of_measured_* = its algorithmic rate over them; roofline.measured_peak is the read "
+                             "or MFMA-loop rate"},
         "parts": part_info,
         "parts_note": ("marked_us: HIP events at every call boundary over a pass of K steps, each marker adding a "
                        "dispatch gap; us: marked_us less the mean gap (the marked pass's excess over the unmarked "
