@@ -176,11 +176,13 @@ hipError_t launch_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint1
 int gqa_head_blocks(int hkv) { return (hkv + 3) / 4; }
 int gqa_choose_path(int rows, int path);
 bool gqa_tg_ok(int d, int rows);
+bool gqa_tg_auto(int d, int hkv, int rows);
 
 // Launch shape of the head-block MFMA kernel (the shapes the token-group
-// kernel does not take: d = 64, and more rows per KV head than one of its
-// waves holds): KV heads per block, row-group waves per head and 16-row blocks
-// per wave. The default block holds kBase heads with
+// kernel does not take: more rows per KV head than one of its waves holds, and
+// d = 64 with KV heads in whole eights under the automatic split): KV heads
+// per block, row-group waves per head and 16-row blocks per wave. The default
+// block holds kBase heads with
 // one wave each (all rows of a head in that wave); when hkv is not a multiple
 // of kBase, or a head has more rows than one wave holds, a block takes the
 // fewest heads a whole LDS token row allows (kMin) and spreads each head's
@@ -248,7 +250,7 @@ int gqa_workers(int b, int hkv, int d, int rows, int path, int t_max, int reques
 {
     if (requested > 0) return requested;
     int w;
-    if (gqa_choose_path(rows, path) == 1 && gqa_tg_ok(d, rows)) {
+    if (gqa_choose_path(rows, path) == 1 && gqa_tg_auto(d, hkv, rows)) {
         // token-group kernel: one block (worker, KV head) per CU
         w = current_cu_count() / hkv;
     } else if (gqa_choose_path(rows, path) == 0) {
@@ -374,10 +376,18 @@ hipError_t dispatch_gqa_mfma(const GqaGeom &g, const GqaArgs &a)
 // ---- token-group kernel: one block per (sequence, KV head), no split-KV
 constexpr int kGqaTgNst = 2;
 
-bool gqa_tg_ok(int d, int rows) { return (d == 128 && rows <= 64) || (d == 256 && rows <= 32); }
+bool gqa_tg_ok(int d, int rows) { return ((d == 64 || d == 128) && rows <= 64) || (d == 256 && rows <= 32); }
 
-// Waves per block: about 32 KB of stage copies in flight per CU (one 16-token
-// stage per wave: four waves per CU at d = 128, two at d = 256) measured
+// The token-group kernel under the automatic worker count. At d = 64 with KV
+// heads in whole eights the head-block kernel stays: its blocks copy all eight
+// heads' 1 KB token rows whole, where a token-group block reads its own head's
+// 128 bytes of every 1 KB (measured, hq = 32, hkv = 8: b = 64, t = 4096 84.5
+// against 91.5 us; b = 8, t = 32768 84.5 against 95.3; b = 32, t = 4096 even).
+// With four KV heads or fewer the token-group kernel is about twice as fast.
+bool gqa_tg_auto(int d, int hkv, int rows) { return gqa_tg_ok(d, rows) && !(d == 64 && hkv % 8 == 0); }
+
+// Waves per block: about 32 KB of stage copies in flight per CU (one stage per
+// wave, 8 KB at d = 64 and 128: four waves per CU; 16 KB at d = 256: two) measured
 // fastest at every batch shape tried (per call, 0.54 GB of K/V unless noted):
 //   d = 128, b*hkv =  256: 4 waves 82.5 us, 2 waves 100.7, 1 wave 176
 //   d = 128, b*hkv =  512: 2 waves 87-89, 4 waves 91-93 (MHA, 1.07 GB: 165 vs 178)
@@ -386,7 +396,7 @@ bool gqa_tg_ok(int d, int rows) { return (d == 128 && rows <= 64) || (d == 256 &
 //   d = 256, b*hkv =  512: 1 wave 82.5, 2 waves 85.5, 4 waves 86.5
 int gqa_tg_waves(int units, int d)
 {
-    const int per_cu = d == 128 ? 4 : 2;  // waves per CU for ~32 KB in flight
+    const int per_cu = d == 256 ? 2 : 4;  // waves per CU for ~32 KB in flight
     const long budget = 3L * per_cu * current_cu_count();
     for (int tg = 4; tg > 1; tg >>= 1)
         if (2L * tg * units <= budget) return tg;
@@ -424,7 +434,14 @@ hipError_t launch_gqa_tg_waves(int tg, const GqaArgs &a)
 hipError_t dispatch_gqa_tg(int d, int rows, int tg, const GqaArgs &a)
 {
     const int nrb = (rows + 15) / 16;
-    if (d == 128) {
+    if (d == 64) {
+        switch (nrb) {
+        case 1: return launch_gqa_tg_waves<64, 1>(tg, a);
+        case 2: return launch_gqa_tg_waves<64, 2>(tg, a);
+        case 3: return launch_gqa_tg_waves<64, 3>(tg, a);
+        case 4: return launch_gqa_tg_waves<64, 4>(tg, a);
+        }
+    } else if (d == 128) {
         switch (nrb) {
         case 1: return launch_gqa_tg_waves<128, 1>(tg, a);
         case 2: return launch_gqa_tg_waves<128, 2>(tg, a);
@@ -629,7 +646,8 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
     // a null workspace: one worker per sequence (one split), num_workers ignored.
     // The token-group kernel takes that mode where its shapes allow, and also
     // the automatic one when the batch gives every CU a (sequence, KV head).
-    const bool tg = use_mfma && gqa_tg_ok(d, rows);
+    const bool tg = use_mfma && (workspace != nullptr && num_workers == 0 ? gqa_tg_auto(d, hkv, rows)
+                                                                          : gqa_tg_ok(d, rows));
     const bool per_seq =
         workspace == nullptr || (tg && num_workers == 0 && (long)b * hkv >= current_cu_count());
     const int workers = per_seq ? b : gqa_workers(b, hkv, d, rows, path, t_max, num_workers);

@@ -356,6 +356,15 @@ __device__ __forceinline__ int gqa_swz(int t)
     return t ^ ((t & 1) << 2) ^ ((((t >> 1) ^ t) & 1) << 3);
 }
 
+// The same for token rows of 128 bytes (one head of d = 64: eight chunks, two
+// rows per 256-byte bank line). Checked on the CPU: the 16-token score reads
+// (a 16-lane pass per chunk) and the 4-token transposing reads (32-lane
+// passes) touch every bank at most once. Bits 1..3 of the token, permuted.
+__device__ __forceinline__ int gqa_swz64(int t)
+{
+    return (((t >> 1) & 3) << 1) | ((t >> 3) & 1);
+}
+
 
 template <int D, int RBLK, int HPB, int NST, int DV = D, int RG = 1>
 __global__ void __launch_bounds__(64 * HPB * RG, 1)
@@ -621,7 +630,7 @@ __global__ void __launch_bounds__(64 * HPB * RG, 1)
 //
 // A block is one (worker, KV head). Its worker's cache range is walked piece by
 // piece, a piece being the worker's tiles of one sequence; the TG waves take
-// the piece's 16-token stages round robin (wave w: stages w, w + TG, ...), each
+// the piece's stages (16 tokens, 32 at d = 64) round robin (wave w: stages w, w + TG, ...), each
 // through a ring of its own in LDS, so the loop has no barrier: a wave waits
 // only for its own copies (vmcnt). At the end of a piece the waves' softmax
 // states (reference maximum, sum, unnormalised accumulators) meet in LDS and
@@ -641,9 +650,10 @@ __global__ void __launch_bounds__(64 * HPB * RG, 1)
 // the waves per block for about 32 KB in flight per CU).
 template <int D, int RBLK, int TG, int NST>
 struct GqaTgCfg {
-    static_assert(D == 128 || D == 256, "head dim");
+    static_assert(D == 64 || D == 128 || D == 256, "head dim");
     static_assert(RBLK >= 1 && RBLK <= 4, "one to four 16-row blocks per wave");
-    static constexpr int T = 16;                    // tokens per stage
+    static constexpr int T = D == 64 ? 32 : 16;     // tokens per stage: 8 KB of K and V at d = 64 and 128
+    static constexpr int NSUB = T / 16;             // 16-token MFMA blocks per stage
     static constexpr int ROW = D * 2;               // bytes of one head's K (or V) token row
     static constexpr int CPR = ROW / 16;            // 16-byte chunks per token row
     static constexpr int STAGE_BYTES = 2 * T * ROW; // T K rows, then T V rows
@@ -656,6 +666,7 @@ struct GqaTgCfg {
     static constexpr int LDS_BYTES = TG * RING > MERGE_BYTES ? TG * RING : MERGE_BYTES;
     static constexpr int KS = D / 32, DB = D / 16;
     static_assert(kGqaTile % T == 0, "planner tiles are whole stages");
+    static_assert(LW % 2 == 0 && LWK * 64 == T * CPR, "the K rows fill whole copy instructions");
     static_assert(NST >= 2 && (NST - 2) * LW <= 63, "outstanding copies fit the vmcnt counter");
     static_assert(LDS_BYTES <= 163840, "LDS of a CU");
 };
@@ -669,6 +680,7 @@ __global__ void __launch_bounds__(64 * TG, 1)
                   float *__restrict__ lse, uint16_t *__restrict__ part_out, float *__restrict__ part_lse)
 {
     using C = GqaTgCfg<D, RBLK, TG, NST>;
+    auto swz = [](int t) { return D == 64 ? gqa_swz64(t) : gqa_swz(t); };
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     DA_LDS char *lds = (DA_LDS char *)smem;
     const int unit = xcd_linear_unit(blockIdx.x, gridDim.x);
@@ -729,11 +741,14 @@ __global__ void __launch_bounds__(64 * TG, 1)
     DA_LDS char *ring = lds + w * C::RING;
     const int tok_e = hkv * D;  // elements of one token's K (or V) row, all KV heads
     const int qk_base = n * C::ROW;
-    const int sq = gqa_swz(n);
+    const int sq = swz(n);
     const int tr_tok = 4 * g + (n >> 2);
-    const int st = gqa_swz(tr_tok);
+    const int st = swz(tr_tok);
     const int hsel = (n & 3) >> 1;
     const int tr_base = C::T * C::ROW + tr_tok * C::ROW + ((n & 1) << 3);
+    // a stage's second 16-token block (d = 64) lies 16 rows further on; both swizzles depend
+    // only on a token's place within its block of 16, so sq and st serve every block
+    constexpr int SUBB = 16 * C::ROW;
 
     // One piece: the stages [tok0_piece, tok0_piece + 16 * nall) of sequence bq,
     // merged at the end into the rows' result (final) or into partial slot sl.
@@ -749,7 +764,7 @@ __global__ void __launch_bounds__(64 * TG, 1)
                 const bool is_k = i < C::LWK;
                 const int p = (is_k ? i : i - C::LWK) * 64 + lane;  // chunk of the K (or V) rows
                 const int tk = p / C::CPR;
-                const int c = (p - tk * C::CPR) ^ gqa_swz(tk);
+                const int c = (p - tk * C::CPR) ^ swz(tk);
                 // rows past L read as zero (out of range: no memory request)
                 const uint32_t off = (uint32_t)(((tok0 + tk) * tok_e + kvh * D) * 2 + c * 16);
                 lds_dma16_stream(is_k ? rsrc_k : rsrc_v, dst + i * 1024, off);
@@ -791,15 +806,20 @@ __global__ void __launch_bounds__(64 * TG, 1)
             }
             const int tok0 = tok0_piece + (w + j * TG) * C::T;
             const DA_LDS char *stg = ring + (j % NST) * C::STAGE_BYTES;
-            f32x4 S[RBLK];
+            f32x4 S[C::NSUB][RBLK];
 #pragma unroll
-            for (int rb = 0; rb < RBLK; ++rb) S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int sb = 0; sb < C::NSUB; ++sb)
+#pragma unroll
+                for (int rb = 0; rb < RBLK; ++rb) S[sb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < C::KS; ++kk) {
                 const int c = kk * 4 + g;
-                const bf16x8 a = *(const DA_LDS bf16x8 *)(stg + qk_base + ((c ^ sq) << 4));
 #pragma unroll
-                for (int rb = 0; rb < RBLK; ++rb) S[rb] = mfma16x16x32(a, qB[rb][kk], S[rb]);
+                for (int sb = 0; sb < C::NSUB; ++sb) {
+                    const bf16x8 a = *(const DA_LDS bf16x8 *)(stg + sb * SUBB + qk_base + ((c ^ sq) << 4));
+#pragma unroll
+                    for (int rb = 0; rb < RBLK; ++rb) S[sb][rb] = mfma16x16x32(a, qB[rb][kk], S[sb][rb]);
+                }
             }
             // mask, then a lane-local test whether any reference must move (rare: mostly
             // the first stages of a piece); only then is the row maximum formed across
@@ -808,12 +828,17 @@ __global__ void __launch_bounds__(64 * TG, 1)
             bool need = false;
 #pragma unroll
             for (int rb = 0; rb < RBLK; ++rb) {
-                if (tok0 + C::T > nvis_min) {
+                float mx = -INFINITY;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (tok0 + g * 4 + i >= nvis[rb]) S[rb][i] = -INFINITY;
+                for (int sb = 0; sb < C::NSUB; ++sb) {
+                    if (tok0 + C::T > nvis_min) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (tok0 + sb * 16 + g * 4 + i >= nvis[rb]) S[sb][rb][i] = -INFINITY;
+                    }
+                    mx = fmaxf(mx, fmaxf(fmaxf(S[sb][rb][0], S[sb][rb][1]), fmaxf(S[sb][rb][2], S[sb][rb][3])));
                 }
-                mloc[rb] = fmaxf(fmaxf(S[rb][0], S[rb][1]), fmaxf(S[rb][2], S[rb][3])) * scale_log2;
+                mloc[rb] = mx * scale_log2;
                 need |= mloc[rb] > mref[rb] + kRescaleSlack;
             }
             if (__builtin_amdgcn_ballot_w64(need)) {
@@ -830,26 +855,32 @@ __global__ void __launch_bounds__(64 * TG, 1)
                     }
                 }
             }
-            i16x4 pB[RBLK];
+            i16x4 pB[C::NSUB][RBLK];
 #pragma unroll
             for (int rb = 0; rb < RBLK; ++rb) {
                 const float ms = mref[rb] == -INFINITY ? 0.f : mref[rb];
-                float p[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(S[rb][i], scale_log2, -ms));
-                lsum[rb] += (p[0] + p[1]) + (p[2] + p[3]);
-                const u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-                pB[rb] = __builtin_bit_cast(i16x4, pk);
+                for (int sb = 0; sb < C::NSUB; ++sb) {
+                    float p[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(S[sb][rb][i], scale_log2, -ms));
+                    lsum[rb] += (p[0] + p[1]) + (p[2] + p[3]);
+                    const u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+                    pB[sb][rb] = __builtin_bit_cast(i16x4, pk);
+                }
             }
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-                const int c = 2 * db + hsel;
-                const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (DA_LDS i16x4 *)(stg + tr_base + ((c ^ st) << 4)));
+            for (int sb = 0; sb < C::NSUB; ++sb)
 #pragma unroll
-                for (int rb = 0; rb < RBLK; ++rb)
-                    acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pB[rb], acc[rb][db], 0, 0, 0);
-            }
+                for (int db = 0; db < C::DB; ++db) {
+                    const int c = 2 * db + hsel;
+                    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (DA_LDS i16x4 *)(stg + sb * SUBB + tr_base + ((c ^ st) << 4)));
+#pragma unroll
+                    for (int rb = 0; rb < RBLK; ++rb)
+                        acc[rb][db] =
+                            __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pB[sb][rb], acc[rb][db], 0, 0, 0);
+                }
         }
 
         // ---- merge the token groups: M = max_w m_w, l = sum_w l_w 2^(m_w - M),

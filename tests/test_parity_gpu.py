@@ -381,7 +381,7 @@ def test_gqa_null_workspace(da, oracle_mod, case, path):
 GQA_TOKEN_GROUPS = [
     # (b, s, hq, hkv, d, t_max): b * hkv >= 256, so the automatic choice (and the null workspace)
     # runs one block per (sequence, KV head) whose waves split the tokens and merge in LDS; the
-    # waves per block (4, 2 or 1) follow from b * hkv and d
+    # waves per block (4, 2 or 1) follow from b * hkv and d; d = 64 takes 32-token stages
     (32, 1, 64, 8, 128, 300),    # the layer's geometry, ragged lengths
     (16, 3, 256, 16, 128, 90),   # group 16 x 3 drafts = 48 rows: three row blocks
     (64, 4, 16, 4, 128, 70),     # 16 rows over four drafts
@@ -391,6 +391,11 @@ GQA_TOKEN_GROUPS = [
     (64, 2, 64, 8, 128, 80),     # 512 blocks: two waves per block
     (256, 1, 8, 4, 128, 40),     # 1024 blocks: one wave per block
     (128, 2, 16, 4, 256, 50),    # d = 256, 512 blocks: one wave per block
+    (32, 1, 32, 8, 64, 300),     # d = 64, 4 rows
+    (64, 4, 64, 4, 64, 70),      # d = 64, 64 rows: four row blocks
+    (32, 3, 40, 8, 64, 90),      # d = 64, 15 rows
+    (128, 2, 16, 4, 64, 50),     # d = 64, 512 blocks: two waves per block
+    (512, 1, 16, 4, 64, 40),     # d = 64, 2048 blocks: one wave per block
 ]
 
 
