@@ -512,6 +512,27 @@ hipError_t launch_unabs(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     return hipGetLastError();
 }
 
+// Per-head projection launch (one block per 64 x BN tile).
+template <int BN>
+hipError_t launch_head_gemm(const uint16_t *a, const uint16_t *bw, uint16_t *c, int m, int h, int n, int k,
+                            hipStream_t stream)
+{
+    using G = da::HeadGemmCfg<BN>;
+    auto kern = da::head_gemm_lds_kernel<BN>;
+    static std::once_flag attr_once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(attr_once, [&] {
+        attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * G::STAGE);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    const int ntm = (m + G::BM - 1) / G::BM, ntn = (n + BN - 1) / BN;
+    const int tiles = h * ntm * ntn;
+    const int lds = (k > G::BK ? 2 : 1) * G::STAGE;  // a second stage buffer only for longer contractions
+    hipLaunchKernelGGL(kern, dim3((tiles + 7) / 8 * 8), dim3(256), lds, stream, a, bw, c, m, h, n, k, ntm, ntn,
+                       tiles);
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -759,30 +780,22 @@ da_status mla_decode_unabsorbed(const uint16_t *q, const uint16_t *k_cache, cons
 }
 
 // ------------------------------------------------------------------ per-head projections
-#ifndef PROJ_BLOCKS_PER_CU
-#define PROJ_BLOCKS_PER_CU 2  // blocks per CU of the tile loop
-#endif
 static da_status head_gemm(const uint16_t *a, const uint16_t *bw, uint16_t *c, int m, int h, int n, int k,
                            void *stream)
 {
     if (!a || !bw || !c || m <= 0 || h <= 0 || n <= 0 || k <= 0) return DA_ERR_INVALID_ARG;
     if (k % 32 != 0) return DA_ERR_UNSUPPORTED;
     if (!aligned16(a) || !aligned16(bw) || !aligned16(c)) return DA_ERR_INVALID_ARG;
-    const long tiles = (long)h * ((n + da::kGemmTile - 1) / da::kGemmTile) * ((m + da::kGemmTile - 1) / da::kGemmTile);
-    const int cus = current_cu_count();
-    if (tiles < 2L * cus) {
-        // few tiles: the four waves of a block split each tile's contraction
-        const long want = 2L * cus;
-        const unsigned grid = (unsigned)(tiles < want ? tiles : want);
-        hipLaunchKernelGGL(da::head_gemm_kernel<4>, dim3(grid), dim3(256), 0, (hipStream_t)stream, a, bw, c, m, h, n,
-                           k);
-    } else {
-        const long want = (long)PROJ_BLOCKS_PER_CU * cus;
-        const long blocks = (tiles + 3) / 4;  // four tiles (one per wave) per block
-        const unsigned grid = (unsigned)(blocks < want ? blocks : want);
-        hipLaunchKernelGGL(da::head_gemm_kernel<1>, dim3(grid), dim3(256), 0, (hipStream_t)stream, a, bw, c, m, h, n,
-                           k);
-    }
+    // a tile's 64 A rows, and its B rows, must be addressable by a 32-bit buffer offset;
+    // the tile count must fit an int
+    if ((long long)64 * h * k * 2 >= (1LL << 31) || (long long)128 * k * 2 >= (1LL << 31)) return DA_ERR_UNSUPPORTED;
+    const long long t128 = (long long)h * ((m + 63) / 64) * ((n + 127) / 128);
+    if (2 * t128 >= (1LL << 31)) return DA_ERR_UNSUPPORTED;
+    // 128-column tiles when they give every CU two blocks, else 64-column ones (twice as many)
+    const hipError_t e = t128 >= 2LL * current_cu_count()
+                             ? launch_head_gemm<128>(a, bw, c, m, h, n, k, (hipStream_t)stream)
+                             : launch_head_gemm<64>(a, bw, c, m, h, n, k, (hipStream_t)stream);
+    if (e != hipSuccess) return DA_ERR_HIP;
     return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_HIP;
 }
 

@@ -597,6 +597,9 @@ PROJ_CASES = [
     ("decompress", 1, 1, 7, 100, 256),   # N = 100: a ragged N tile
     ("absorb", 32, 4, 128, 128, 512),    # DeepSeek-V3-like, s = 4
     ("decompress", 32, 4, 128, 128, 512),
+    ("absorb", 2, 3, 4, 32, 64),         # one k-step
+    ("decompress", 2, 5, 3, 96, 160),    # five k-steps: the load ring wraps part-way
+    ("decompress", 1, 70, 2, 64, 1024),  # 32 k-steps, four per wave in the split form
 ]
 
 
