@@ -183,6 +183,12 @@ def test_projection_contracted_width_multiple_of_32(lib):
     assert lib.mla_decompress_output(FAKE, FAKE, FAKE, 2, 1, 4, 500, 128, None) == 2
 
 
+def test_projection_tile_span_limit(lib):
+    # a 64-row tile's inputs span 64 * h * width * 2 bytes, which must stay below 2^31
+    assert lib.mla_absorb_queries(FAKE, FAKE, FAKE, 2, 1, 1 << 17, 128, 512, None) == 2
+    assert lib.mla_decompress_output(FAKE, FAKE, FAKE, 2, 1, 1 << 15, 512, 128, None) == 2
+
+
 def split_call(lib, **kw):
     a = dict(b=2, s=2, h=8, o=256, n=64, scale=0.1, ws=FAKE, wsb=0, nw=0, qn=FAKE)
     a.update(kw)
