@@ -320,6 +320,7 @@ struct GqaArgs {
     float *part_lse;
     int workers;
     hipStream_t stream;
+    int rsplit = 1;  // token-group kernel: blocks that split a KV head's query rows
 };
 
 template <int D, int RBLK, int HPB, int RG>
@@ -386,6 +387,19 @@ bool gqa_tg_ok(int d, int rows) { return ((d == 64 || d == 128) && rows <= 64) |
 // With four KV heads or fewer the token-group kernel is about twice as fast.
 bool gqa_tg_auto(int d, int hkv, int rows) { return gqa_tg_ok(d, rows) && !(d == 64 && hkv % 8 == 0); }
 
+// Row splits of the token-group kernel. With one KV head for all query heads
+// (MQA) and more than 48 query rows (d = 64 or 128), the rows are split over
+// two blocks that read the same K/V, consecutive units on one XCD: a wave then
+// holds 32 rows at most, its registers allow two waves per SIMD, and those
+// overlap one another's arithmetic and copy waits. Measured per call (b = 32,
+// hq = 64, t = 4096): d = 128 25.2-25.8 against 27.7-28.1 us, d = 64 16.0-16.4
+// against 18.2-18.6; at hq = 48 the split was slower (23.9-24.3 against
+// 23.3-24.3). With several KV heads the two blocks of a pair drift apart over
+// their longer streams and read the K/V twice from HBM: b = 8, s = 4, hq = 128,
+// hkv = 8, t = 16384 126 against 93-97 us; b = 32, s = 8, hq = 64, hkv = 8,
+// t = 2048 60 against 49-55.
+int gqa_tg_rsplit(int d, int hkv, int rows) { return d <= 128 && hkv == 1 && rows > 48 ? 2 : 1; }
+
 // Waves per block: about 32 KB of stage copies in flight per CU (one stage per
 // wave, 8 KB at d = 64 and 128: four waves per CU; 16 KB at d = 256: two) measured
 // fastest at every batch shape tried (per call, 0.54 GB of K/V unless noted):
@@ -414,14 +428,14 @@ hipError_t launch_gqa_tg(const GqaArgs &a)
         attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     });
     if (attr_err != hipSuccess) return attr_err;
-    const int units = a.workers * a.hkv;
+    const int units = a.workers * a.hkv * a.rsplit;
     const int grid = (units + 7) / 8 * 8;
     if (log_plan())
-        fprintf(stderr, "[decode_attn] gqa-token-groups d=%d row blocks=%d workers=%d blocks=%d waves=%d lds=%d\n", D,
-                RBLK, a.workers, units, TG, C::LDS_BYTES);
+        fprintf(stderr, "[decode_attn] gqa-token-groups d=%d row blocks=%d row splits=%d workers=%d blocks=%d waves=%d lds=%d\n",
+                D, RBLK, a.rsplit, a.workers, units, TG, C::LDS_BYTES);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * TG), C::LDS_BYTES, a.stream, a.q, a.k, a.v, a.seqlens, a.b, a.s,
-                       a.hq, a.hkv, a.t_max, a.scale_log2, units, a.hdr, a.tile_start, a.slot_start, a.out, a.lse,
-                       a.part_out, a.part_lse);
+                       a.hq, a.hkv, a.t_max, a.scale_log2, a.rsplit, units, a.hdr, a.tile_start, a.slot_start, a.out,
+                       a.lse, a.part_out, a.part_lse);
     return hipSuccess;
 }
 
@@ -689,10 +703,11 @@ da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
                 hkv, t_max, workers, use_mfma ? "mfma" : "valu");
     bool ok = false;
     if (use_mfma) {
+        const int rsplit = tg ? gqa_tg_rsplit(d, hkv, rows) : 1;
         const GqaArgs a{q, k_cache, v_cache, seqlens, b, s, hq, hkv, t_max, sl2, out, lse, hdr,
-                        tile_start, slot_start, part_out, part_lse, workers, st_};
+                        tile_start, slot_start, part_out, part_lse, workers, st_, rsplit};
         const GqaGeom g = gqa_geom(d, hkv, rows);
-        const hipError_t e = tg ? dispatch_gqa_tg(d, rows, gqa_tg_waves(workers * hkv, d), a)
+        const hipError_t e = tg ? dispatch_gqa_tg(d, (rows + rsplit - 1) / rsplit, gqa_tg_waves(workers * hkv, d), a)
                              : d == 64 ? dispatch_gqa_mfma<64>(g, a)
                              : d == 128 ? dispatch_gqa_mfma<128>(g, a)
                                         : dispatch_gqa_mfma<256>(g, a);

@@ -643,6 +643,11 @@ __global__ void __launch_bounds__(64 * HPB * RG, 1)
 // automatically when the batch alone has a block for every CU
 // (b * hkv >= CUs).
 //
+// A KV head's query rows may be split over rsplit blocks (rows [rsp * RP,
+// rsp * RP + R) of the head in block rsp), which read the same K/V; the host
+// takes that for MQA with more than 48 rows, which in one wave would leave one
+// wave per SIMD.
+//
 // Ring depth: two stages per wave (one in flight while the other is computed).
 // At the layer's geometry (b = 32, hkv = 8, d = 128, t = 4096; four waves per
 // block) that measured 81.4-81.9 us per call against 86.7-88.4 with three
@@ -675,7 +680,7 @@ template <int D, int RBLK, int TG, int NST>
 __global__ void __launch_bounds__(64 * TG, 1)
     gqa_tg_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
                   const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens, int B, int s, int hq,
-                  int hkv, int t_max, float scale_log2, int units, PlanHeader *__restrict__ hdr,
+                  int hkv, int t_max, float scale_log2, int rsplit, int units, PlanHeader *__restrict__ hdr,
                   int *__restrict__ tile_start, int *__restrict__ slot_start, uint16_t *__restrict__ out,
                   float *__restrict__ lse, uint16_t *__restrict__ part_out, float *__restrict__ part_lse)
 {
@@ -685,20 +690,27 @@ __global__ void __launch_bounds__(64 * TG, 1)
     DA_LDS char *lds = (DA_LDS char *)smem;
     const int unit = xcd_linear_unit(blockIdx.x, gridDim.x);
     if (unit >= units) return;
-    const int worker = unit / hkv;
-    const int kvh = unit - worker * hkv;
-    const int workers = units / hkv;
+    // unit = (worker, KV head, row split): the rsplit blocks of one (worker, KV head) are
+    // consecutive units, hence on one XCD, and read the same K/V rows through its L2
+    const int per_worker = hkv * rsplit;
+    const int worker = unit / per_worker;
+    const int kvh = (unit - worker * per_worker) / rsplit;
+    const int rsp = unit - worker * per_worker - kvh * rsplit;
+    const int workers = units / per_worker;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // token group
     const int lane = tid & 63;
     const int n = lane & 15;
     const int g = lane >> 4;
     const int grp = hq / hkv;
-    const int R = grp * s;  // query rows of this KV head
-    const int M = s * hq;   // query rows per sequence
+    const int RP = (grp * s + rsplit - 1) / rsplit;  // query rows of this KV head per split
+    const int r_base = rsp * RP;                     // this block's first row of the head
+    const int R = min(RP, grp * s - r_base);         // and its row count (>= 1)
+    const int M = s * hq;                            // query rows per sequence
+    // block row r is row r_base + r of the KV head: draft i, query head kvh * grp + j
     auto row_of = [&](int r) {
-        const int i = r / grp;
-        const int j = r - i * grp;
+        const int i = (r_base + r) / grp;
+        const int j = r_base + r - i * grp;
         return i * hq + kvh * grp + j;
     };
 
@@ -786,7 +798,7 @@ __global__ void __launch_bounds__(64 * TG, 1)
         for (int rb = 0; rb < RBLK; ++rb) {
             const int r = rb * 16 + n;
             const bool ok = r < R;
-            nvis[rb] = ok ? L - s + r / grp + 1 : 0;  // causal: draft i sees L - s + i + 1 rows
+            nvis[rb] = ok ? L - s + (r_base + r) / grp + 1 : 0;  // causal: draft i sees L - s + i + 1 rows
             mn = min(mn, nvis[rb]);
             mref[rb] = -INFINITY;
             lsum[rb] = 0.f;

@@ -379,9 +379,10 @@ def test_gqa_null_workspace(da, oracle_mod, case, path):
 
 
 GQA_TOKEN_GROUPS = [
-    # (b, s, hq, hkv, d, t_max): b * hkv >= 256, so the automatic choice (and the null workspace)
-    # runs one block per (sequence, KV head) whose waves split the tokens and merge in LDS; the
-    # waves per block (4, 2 or 1) follow from b * hkv and d; d = 64 takes 32-token stages
+    # (b, s, hq, hkv, d, t_max): with b * hkv >= 256 the automatic choice (and always the null
+    # workspace) runs one block per (sequence, KV head) whose waves split the tokens and merge in
+    # LDS; the waves per block (4, 2 or 1) follow from b * hkv and d; d = 64 takes 32-token
+    # stages; MQA with more than 48 rows splits them over two blocks
     (32, 1, 64, 8, 128, 300),    # the layer's geometry, ragged lengths
     (16, 3, 256, 16, 128, 90),   # group 16 x 3 drafts = 48 rows: three row blocks
     (64, 4, 16, 4, 128, 70),     # 16 rows over four drafts
@@ -396,6 +397,10 @@ GQA_TOKEN_GROUPS = [
     (32, 3, 40, 8, 64, 90),      # d = 64, 15 rows
     (128, 2, 16, 4, 64, 50),     # d = 64, 512 blocks: two waves per block
     (512, 1, 16, 4, 64, 40),     # d = 64, 2048 blocks: one wave per block
+    (32, 1, 64, 1, 128, 300),    # MQA, 64 rows: two blocks of 32 rows per KV head
+    (16, 2, 24, 1, 64, 90),      # MQA, d = 64, 48 rows over two drafts: one block
+    (8, 3, 20, 1, 128, 70),      # MQA, 60 rows over three drafts: 30 + 30
+    (8, 1, 56, 1, 64, 50),       # MQA, d = 64, 56 rows: 28 + 28
 ]
 
 
