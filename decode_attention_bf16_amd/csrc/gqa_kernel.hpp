@@ -475,7 +475,8 @@ __global__ void __launch_bounds__(64 * HPB * RG, 1)
             const int te = is_k ? tok_k : tok_v;
             // a head past hkv reads as zero (out of range: no memory request)
             const uint32_t off = c < heads_here * hd
-                                     ? (uint32_t)(((tok0 + tk) * te + hb * C::HPB * hd * 8) * 2 + c * 16)
+                                     ? ((uint32_t)(tok0 + tk) * (uint32_t)te + (uint32_t)(hb * C::HPB * hd * 8)) * 2u +
+                                           (uint32_t)(c * 16)
                                      : 0x80000000u;
             // each K/V byte is read by this wave's block only: a streaming copy
             lds_dma16_stream(is_k ? rsrc_k : rsrc_v, dst + cp * 1024, off);
@@ -778,7 +779,9 @@ __global__ void __launch_bounds__(64 * TG, 1)
                 const int tk = p / C::CPR;
                 const int c = (p - tk * C::CPR) ^ swz(tk);
                 // rows past L read as zero (out of range: no memory request)
-                const uint32_t off = (uint32_t)(((tok0 + tk) * tok_e + kvh * D) * 2 + c * 16);
+                // unsigned: padding rows of a sequence at the size limit pass 2^31 bytes
+                const uint32_t off =
+                    ((uint32_t)(tok0 + tk) * (uint32_t)tok_e + (uint32_t)(kvh * D)) * 2u + (uint32_t)(c * 16);
                 lds_dma16_stream(is_k ? rsrc_k : rsrc_v, dst + i * 1024, off);
             }
         };

@@ -701,6 +701,36 @@ def test_mla_split_cache(da, oracle_mod, case):
     compare(out.cpu(), lse.cpu(), ref_o, ref_l, "split cache %s" % (case,))
 
 
+# ------------------------------------------------------------------ the longest sequences the ABI takes
+def test_mla_longest_sequence(da, oracle_mod):
+    """One sequence whose cache is just under 2^31 bytes, the limit of the 32-bit buffer offsets
+    (t_max * (k + p) * 2 < 2^31: 1,864,135 rows, the last tile ragged), every row: split over the
+    automatic worker count (one row block, so the block-per-row combine) and, with no workspace,
+    walked by a single block. Inputs drawn on the GPU."""
+    t = ((1 << 31) - 1) // ((512 + 64) * 2)
+    shape = mla_shape(1, 2, 8, 512, 64, t, seed=91)
+    tensors = wl.make_mla(shape, device=dev())
+    ref_o, ref_l = oracle_mod.mla(*[x.cpu() for x in tensors], shape.scale)
+    for null_ws in (False, True):
+        print("mla longest sequence t=%d null_workspace=%s" % (t, null_ws), flush=True)
+        out, lse = run_mla(da, shape, tensors, 0, null_workspace=null_ws)
+        compare(out, lse, ref_o, ref_l, "mla t=%d null_ws=%s" % (t, null_ws))
+
+
+def test_gqa_longest_sequence(da, oracle_mod):
+    """One sequence whose K (and V) rows are just under 2^31 bytes (t_max * hkv * d * 2 < 2^31:
+    4,194,303 rows at hkv = 2, d = 128), every row: the token-group kernel under the automatic
+    split and with no workspace (one block per KV head). Inputs drawn on the GPU."""
+    t = ((1 << 31) - 1) // (2 * 128 * 2)
+    shape = wl.GQAShape(b=1, s=1, hq=16, hkv=2, d=128, t_max=t, scale=1.0 / math.sqrt(128), seed=92)
+    tensors = wl.make_gqa(shape, device=dev())
+    ref_o, ref_l = oracle_mod.gqa(*[x.cpu() for x in tensors], shape.scale)
+    for null_ws in (False, True):
+        print("gqa longest sequence t=%d null_workspace=%s" % (t, null_ws), flush=True)
+        out, lse = run_gqa(da, shape, tensors, 0, null_workspace=null_ws)
+        compare(out, lse, ref_o, ref_l, "gqa t=%d null_ws=%s" % (t, null_ws))
+
+
 @pytest.fixture(scope="module")
 def gqa_long_case(oracle_mod):
     """One 262,144-token sequence at 24 query / 4 KV heads, d = 256, with the

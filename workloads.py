@@ -9,7 +9,10 @@ float32 values, which are rounded to bf16 (round-to-nearest-even, torch's
 ``.to(torch.bfloat16)``). Draw order: for ragged workloads the sequence lengths
 first (uniform integers), then the query tensors, then the cache tensors (MLA:
 q_lat, q_rope, cache; GQA: q, k, v). Cache rows beyond a sequence's length are
-drawn like the rest (they are never read as valid rows).
+drawn like the rest (they are never read as valid rows). The largest shapes
+(caches of about 2 GB per sequence) are drawn the same way by a generator on
+the GPU (``device=``), whose numbers differ from the CPU generator's for the
+same seed; the oracle then reads a host copy.
 
 Shapes follow the source pages' DeepSeek-V3-like geometry ("Mla Analysis"
 skill page, "Cost Models" and "Tensor Shapes": h=128, k=512, p=64, t=4096,
@@ -98,34 +101,36 @@ WORKLOADS = {
 
 
 def _normal_bf16(gen: torch.Generator, shape) -> torch.Tensor:
-    return torch.randn(*shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    return torch.randn(*shape, generator=gen, dtype=torch.float32, device=gen.device).to(torch.bfloat16)
 
 
 def _seqlens(gen: torch.Generator, b: int, t_max: int, ragged) -> torch.Tensor:
     if ragged is None:
-        return torch.full((b,), t_max, dtype=torch.int32)
+        return torch.full((b,), t_max, dtype=torch.int32, device=gen.device)
     lo, hi = ragged
-    return torch.randint(lo, hi + 1, (b,), generator=gen, dtype=torch.int64).to(torch.int32)
+    return torch.randint(lo, hi + 1, (b,), generator=gen, dtype=torch.int64, device=gen.device).to(torch.int32)
 
 
-def make_mla(shape: MLAShape, seqlens=None):
-    """Return (q_lat, q_rope, cache, seqlens) as CPU tensors (bf16, bf16, bf16, int32)."""
-    gen = torch.Generator().manual_seed(shape.seed)
+def make_mla(shape: MLAShape, seqlens=None, device=None):
+    """Return (q_lat, q_rope, cache, seqlens) as CPU tensors (bf16, bf16, bf16, int32),
+    or, with ``device``, drawn by a generator on that device and left there (seqlens too)."""
+    gen = torch.Generator(device=device if device is not None else "cpu").manual_seed(shape.seed)
     sl = _seqlens(gen, shape.b, shape.t_max, shape.ragged)
     if seqlens is not None:
-        sl = torch.as_tensor(seqlens, dtype=torch.int32).clone()
+        sl = torch.as_tensor(seqlens, dtype=torch.int32).clone().to(gen.device)
     q_lat = _normal_bf16(gen, (shape.b, shape.s, shape.h, shape.k))
     q_rope = _normal_bf16(gen, (shape.b, shape.s, shape.h, shape.p))
     cache = _normal_bf16(gen, (shape.b, shape.t_max, shape.k + shape.p))
     return q_lat, q_rope, cache, sl
 
 
-def make_gqa(shape: GQAShape, seqlens=None):
-    """Return (q, k, v, seqlens) as CPU tensors (bf16 x3, int32)."""
-    gen = torch.Generator().manual_seed(shape.seed)
+def make_gqa(shape: GQAShape, seqlens=None, device=None):
+    """Return (q, k, v, seqlens) as CPU tensors (bf16 x3, int32), or, with ``device``,
+    drawn by a generator on that device and left there (seqlens too)."""
+    gen = torch.Generator(device=device if device is not None else "cpu").manual_seed(shape.seed)
     sl = _seqlens(gen, shape.b, shape.t_max, shape.ragged)
     if seqlens is not None:
-        sl = torch.as_tensor(seqlens, dtype=torch.int32).clone()
+        sl = torch.as_tensor(seqlens, dtype=torch.int32).clone().to(gen.device)
     q = _normal_bf16(gen, (shape.b, shape.s, shape.hq, shape.d))
     k = _normal_bf16(gen, (shape.b, shape.t_max, shape.hkv, shape.d))
     v = _normal_bf16(gen, (shape.b, shape.t_max, shape.hkv, shape.d))
