@@ -493,12 +493,12 @@ def test_gqa_many_segments_per_row(da, oracle_mod, case, path):
 
 
 # ------------------------------------------------------------------ un-absorbed MLA (per-head K and V)
-def unabsorbed_inputs(b, s, h, t, seqlens, seed):
-    gen = torch.Generator().manual_seed(seed)
-    q = torch.randn((b, s, h, 192), generator=gen).to(torch.bfloat16)
-    k = torch.randn((b, t, h, 192), generator=gen).to(torch.bfloat16)
-    v = torch.randn((b, t, h, 128), generator=gen).to(torch.bfloat16)
-    return q, k, v, torch.tensor(seqlens, dtype=torch.int32)
+def unabsorbed_inputs(b, s, h, t, seqlens, seed, device="cpu"):
+    gen = torch.Generator(device=device).manual_seed(seed)
+    q = torch.randn((b, s, h, 192), generator=gen, device=device).to(torch.bfloat16)
+    k = torch.randn((b, t, h, 192), generator=gen, device=device).to(torch.bfloat16)
+    v = torch.randn((b, t, h, 128), generator=gen, device=device).to(torch.bfloat16)
+    return q, k, v, torch.tensor(seqlens, dtype=torch.int32, device=device)
 
 
 def unabsorbed_reference(oracle_mod, q, k, v, sl, scale):
@@ -547,6 +547,24 @@ def test_mla_unabsorbed_small(da, oracle_mod, case, null_ws):
     torch.cuda.synchronize()
     ref_o, ref_l = unabsorbed_reference(oracle_mod, q, k, v, sl, scale)
     compare(out.cpu(), lse.cpu(), ref_o, ref_l, "mla unabsorbed %s" % (case,))
+
+
+def test_mla_unabsorbed_longest_sequence(da, oracle_mod):
+    """One sequence whose per-head keys are just under 2^31 bytes (t_max * h * 192 * 2 < 2^31:
+    2,796,202 rows at h = 2), every row, with the automatic workers and with no workspace.
+    Inputs drawn on the GPU."""
+    b, s, h = 1, 2, 2
+    t = ((1 << 31) - 1) // (h * 192 * 2)
+    q, k, v, slt = unabsorbed_inputs(b, s, h, t, [t], seed=93, device=dev())
+    scale = 1.0 / math.sqrt(192)
+    ref_o, ref_l = unabsorbed_reference(oracle_mod, q.cpu(), k.cpu(), v.cpu(), slt.cpu(), scale)
+    for null_ws in (False, True):
+        print("mla unabsorbed longest sequence t=%d null_workspace=%s" % (t, null_ws), flush=True)
+        out = torch.full((b, s, h, 128), float("nan"), dtype=torch.bfloat16, device=dev())
+        lse = torch.full((b, s, h), float("nan"), dtype=torch.float32, device=dev())
+        da.mla_decode_unabsorbed(q, k, v, slt, scale, out=out, lse=lse, null_workspace=null_ws)
+        torch.cuda.synchronize()
+        compare(out.cpu(), lse.cpu(), ref_o, ref_l, "mla unabsorbed t=%d null_ws=%s" % (t, null_ws))
 
 
 def test_mla_unabsorbed_full_heads(da, oracle_mod):
