@@ -417,11 +417,11 @@ int gqa_tg_waves(int units, int d)
     return 1;
 }
 
-template <int D, int RBLK, int TG>
+template <int D, int RBLK, int TG, bool SHARED = false>
 hipError_t launch_gqa_tg(const GqaArgs &a)
 {
     using C = da::GqaTgCfg<D, RBLK, TG, kGqaTgNst>;
-    auto kern = da::gqa_tg_kernel<D, RBLK, TG, kGqaTgNst>;
+    auto kern = da::gqa_tg_kernel<D, RBLK, TG, kGqaTgNst, SHARED>;
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(attr_once, [&] {
@@ -442,6 +442,12 @@ hipError_t launch_gqa_tg(const GqaArgs &a)
 template <int D, int RBLK>
 hipError_t launch_gqa_tg_waves(int tg, const GqaArgs &a)
 {
+    // split rows (MQA): at most 32 rows per block, two row blocks
+    if constexpr (RBLK == 2 && D <= 128)
+        if (a.rsplit > 1)
+            return tg == 4   ? launch_gqa_tg<D, RBLK, 4, true>(a)
+                   : tg == 2 ? launch_gqa_tg<D, RBLK, 2, true>(a)
+                             : launch_gqa_tg<D, RBLK, 1, true>(a);
     return tg == 4 ? launch_gqa_tg<D, RBLK, 4>(a) : tg == 2 ? launch_gqa_tg<D, RBLK, 2>(a) : launch_gqa_tg<D, RBLK, 1>(a);
 }
 
