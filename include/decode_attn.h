@@ -155,13 +155,14 @@ size_t gqa_decode_workspace_size(int b, int s, int hq, int hkv, int d, int t_max
  * (rows padded to blocks of 16, spread over up to four waves per K/V head
  * that share its cache reads), 0 = automatic (currently the MFMA kernel for
  * every R). Both give the same result up to rounding. Workspace as for
- * mla_decode (NULL allowed). With the MFMA kernel, d = 128 (R <= 64) or
- * d = 256 (R <= 32), and either a NULL workspace or num_workers == 0 with
+ * mla_decode (NULL allowed). With the MFMA kernel, d = 64 or 128 (R <= 64)
+ * or d = 256 (R <= 32), and either a NULL workspace or num_workers == 0 with
  * b * hkv at least the device's compute-unit count, no sequence is split:
  * one block per (sequence, K/V head) splits the tokens over its waves and
- * writes the rows itself, and the workspace is not touched. The automatic
- * choice assumes sequences near t_max; pass num_workers > 0 to balance a
- * batch of very unequal lengths over split-KV workers instead.
+ * writes the rows itself, and the workspace is not touched (at d = 64 with
+ * hkv a multiple of 8 the automatic choice keeps the split form instead).
+ * The automatic choice assumes sequences near t_max; pass num_workers > 0 to
+ * balance a batch of very unequal lengths over split-KV workers instead.
  */
 da_status gqa_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
                      const int32_t *seqlens, int b, int s, int hq, int hkv, int d, int t_max,
