@@ -83,6 +83,13 @@ struct MlaCfg {
     static constexpr int CB32 = K / (32 * NVW);                 // 32-column output blocks per value wave
     static constexpr int QCH = 2;                               // score k-steps per LDS read chunk
     static constexpr int QPF = 2;                               // chunks in flight ahead of the MFMAs
+    // latent queries of the block's rows, staged once in the space of tile buffers 2 and 3
+    static constexpr int KL = K / 32;                           // k-steps that are latent only
+    static constexpr int QW = K / 8;                            // 16-byte chunks per latent query row
+    static constexpr int QCOPIES = ROWS * QW / 64 / 4;          // copy instructions per score wave
+    static constexpr int QLDS_OFF = 2 * TILE_BYTES;
+    static_assert(ROWS * QW * 16 <= 2 * TILE_BYTES && NBUF == 4, "the query rows fit tile buffers 2 and 3");
+    static_assert(64 % QW == 0, "query rows pack whole copy instructions");
     static constexpr int PBUF_OFF = NBUF * TILE_BYTES;          // [2 slots][2 row blocks][2 halves][64 lanes] x 16 B
     static constexpr int MREF_OFF = PBUF_OFF + 2 * 4 * 64 * 16;   // [2 slots][2 halves][64 rows] float
     static constexpr int FLAG_OFF = MREF_OFF + 2 * 2 * 64 * 4;    // [2 slots][4 score waves] int
@@ -108,6 +115,18 @@ __device__ __forceinline__ int tile_swz(int r)
 {
     const int i0 = (r >> 1) & 1, i1 = (r >> 2) & 1, i2 = (r >> 3) & 1;
     return i0 | ((i1 ^ i2) << 1) | ((i0 ^ i2) << 2);
+}
+
+// Chunk swizzle of the staged latent query rows (QW 16-byte chunks each): chunk
+// c of row r is stored at c ^ qlat_swz(r). Rows of 256 bytes or more all start
+// on the same bank, so the low four bits take r mod 16; rows of 128 bytes (QW =
+// 8) alternate between the two bank halves, so bits 1..3 of r pick the chunk.
+// Either way the 16 lanes reading one chunk of 16 consecutive rows touch every
+// bank once.
+template <int QW>
+__device__ __forceinline__ int qlat_swz(int r)
+{
+    return QW >= 16 ? (r & 15) : ((r >> 1) & 7);
 }
 
 // Eight bf16 values times a power of two (exact unless the result leaves the
@@ -145,6 +164,15 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
     // rows directly; otherwise one wave writes the plan as arrays for the
     // combine kernel, and every wave derives its own view of it.
     const bool per_seq = hdr == nullptr;
+    // The first segment's latent queries are staged through LDS (below) when every query
+    // row block is read by four or more workers (split-KV with workers >= 4 b): their
+    // copies then mostly hit L2 and land well before the direct loads would. The staging
+    // holds back the third tile's copy until the queries are read out of its buffer, which
+    // costs more than it gains where the queries come from HBM. Measured per call: s = 1,
+    // b = 32, h = 128 (four workers per sequence) 47.7-47.8 against 49.7-49.8 us; one worker
+    // per sequence (s = 4) 141.6-146.1 against 140.3-141.4; ragged b = 64 (two per
+    // sequence) 384.4-385.3 against 380.0-382.4.
+    const bool stage_q = !per_seq && workers >= 4 * B;
     if (!per_seq && unit == 0 && threadIdx.x < 64)
         write_plan(seqlens, B, t_max, C::T, workers, hdr, tile_start, slot_start);
     PlanWalk plan;
@@ -201,13 +229,15 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
         int nvis[2] = {0, 0}, nvis_min = 0;
         PlanWalk cur = plan;
         // a segment starts: its rows' queries, visible lengths and fresh softmax state
-        auto start_segment = [&]() {
+        // (lat_in_lds: the latent k-steps' queries come from LDS instead, below)
+        auto start_segment = [&](bool lat_in_lds) {
             const int L = clamp_len(seqlens[cur.b], t_max);
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
                 nvis[rr] = row_ok[rr] ? (L - s + row[rr] / h + 1) : 0;
 #pragma unroll
                 for (int kk = 0; kk < C::KSTEPS; ++kk) {
+                    if (lat_in_lds && kk < C::KL) continue;
                     u32x4 v = {0u, 0u, 0u, 0u};
                     const int e0 = kk * 32 + g * 8;
                     if (row_ok[rr]) {
@@ -227,9 +257,37 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
             for (int off = 1; off < 64; off <<= 1) mn = min(mn, __shfl_xor(mn, off));
             nvis_min = mn;
         };
-        start_segment();  // the first queries load while the first tiles are copied
-
-        lds_barrier();  // tile 0 has landed
+        if (stage_q) {
+            // The first segment's latent queries come through LDS: the block's 64 rows are
+            // copied HBM -> LDS whole (a row's 2K bytes in one run; loads straight into the
+            // MFMA operand layout move 16 rows x 64 bytes each), into the space of tile
+            // buffers 2 and 3, which the value waves fill only once the queries are read.
+            // Rows past M read as zeros. Row r's chunk c is stored at c ^ qlat_swz(r).
+            const int r0 = rb * C::ROWS;
+            const u32x4 rq = raw_buffer_rsrc(q_lat + ((size_t)cur.b * M + r0) * K, (uint32_t)(M - r0) * K * 2);
+#pragma unroll
+            for (int it = 0; it < C::QCOPIES; ++it) {
+                const int i = it * 4 + w;
+                const int r = i * (64 / C::QW) + lane / C::QW;
+                const int c = (lane % C::QW) ^ qlat_swz<C::QW>(r);
+                lds_dma16(rq, lds + C::QLDS_OFF + i * 1024, (uint32_t)((r * K + c * 8) * 2));
+            }
+            start_segment(true);  // the rope k-steps' queries: registers
+            wait_vmcnt<0>();
+            lds_barrier();  // every wave's query rows, and tile 0, have landed
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const int rq = rowl + 16 * rr;
+#pragma unroll
+                for (int kk = 0; kk < C::KL; ++kk)
+                    qB[rr][kk] = *(const DA_LDS bf16x8 *)(lds + C::QLDS_OFF + rq * C::QW * 16 +
+                                                          (((kk * 4 + g) ^ qlat_swz<C::QW>(rq)) << 4));
+            }
+            lds_barrier();  // the query rows are read: the value waves may refill that space
+        } else {
+            start_segment(false);  // the first queries load while the first tiles are copied
+            lds_barrier();         // tile 0 has landed
+        }
         for (int j = 0; j <= ntiles; ++j) {
             if (j < ntiles) {
                 const int tt = tile_lo + j;
@@ -239,7 +297,7 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
                 // the partner half's flag of the previous step, consumed after the MFMAs
                 int pflag = 0;
                 if (j > 0 && !new_seg) pflag = flag_buf[(slot ^ 1) * 4 + (w ^ 1)];
-                if (new_seg) start_segment();
+                if (new_seg) start_segment(false);
                 const DA_LDS char *tile = lds + (j % C::NBUF) * C::TILE_BYTES;
 
                 // S^T[16 tokens, 32 rows]. The tile's A fragments are read in
@@ -419,14 +477,24 @@ __global__ void __launch_bounds__((MlaCfg<K, P>::THREADS), 1)
         // the first three tiles before step 0 (buffers 0..2), then tile j+2 in step j >= 1
         issue_tile(0);
         if (ntiles > 1) issue_tile(1);
-        if (ntiles > 2) issue_tile(2);
-        if (ntiles > 2)
-            wait_vmcnt<2 * C::LPW>();
-        else if (ntiles > 1)
-            wait_vmcnt<C::LPW>();
-        else
-            wait_vmcnt<0>();
-        lds_barrier();  // tile 0 has landed
+        if (stage_q) {
+            if (ntiles > 1)
+                wait_vmcnt<C::LPW>();
+            else
+                wait_vmcnt<0>();
+            lds_barrier();  // tile 0 has landed (and the score waves' query rows)
+            lds_barrier();  // the score waves have read their queries: buffer 2 is free
+            if (ntiles > 2) issue_tile(2);
+        } else {
+            if (ntiles > 2) issue_tile(2);
+            if (ntiles > 2)
+                wait_vmcnt<2 * C::LPW>();
+            else if (ntiles > 1)
+                wait_vmcnt<C::LPW>();
+            else
+                wait_vmcnt<0>();
+            lds_barrier();  // tile 0 has landed
+        }
         for (int j = 0; j <= ntiles; ++j) {
             const bool issued = j >= 1 && j + 2 < ntiles;
             bool stored = false;
